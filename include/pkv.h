@@ -1,0 +1,328 @@
+/*
+ * pkv.h -- C ABI of libpkv: paged-KV grouped-query attention on AMD MI355X
+ * (gfx950).
+ *
+ * What it computes.  A refcounted pool of fixed-size KV blocks holds the K
+ * and V rows of many sequences; each sequence reads its rows back through a
+ * page table of block ids.  Per layer, new K/V rows are appended, then query
+ * head h attends with kv head h / (n_heads / n_kv_heads) over all cached rows
+ * plus the new ones, query i sitting at position total_k - n_q + i
+ * (offset-causal), and softmax(Q K^T * scale) V is written into an
+ * [n_q, n_heads * head_dim] output.  ("nx_f32_attn_paged.nx source": header
+ * comment and nx_f32_attn_with_paged; "nx_f32_gqa_attention.nx source":
+ * header comment.)
+ *
+ * Step protocol ("nx_f32_attn_paged.nx source", caller contract in the header
+ * comment; "nx_f32_llama_v4b.nx source", nx_f32_llama_stack_forward_v4b):
+ *   pkv_ensure_append(batch, n)            once per step, before layer 0
+ *   for each layer:
+ *     pkv_append_layer(batch, n, layer, K_new, V_new)
+ *     pkv_attn_paged_decode(...)           (n == 1)  or
+ *     pkv_attn_paged_prefill(..., n_q = n)
+ *   pkv_advance(batch, n)                  once per step, after all layers
+ *
+ * Conventions.
+ *  - Status returns: 0 = OK, otherwise a PKV_ERR_* code.  Functions that
+ *    return an id return it (>= 0) or the negated status code.
+ *  - Every argument check runs before any state change or device work: a
+ *    call that fails leaves the pool exactly as it was.
+ *  - Pointers named *_dev are device pointers; all other pointers are host
+ *    pointers.  The caller owns every buffer it passes and keeps device
+ *    buffers alive until the work enqueued on `stream` has finished.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    All device work of one pool must go to one stream at a time; a call that
+ *    names a different stream than the pool's previous call first waits for
+ *    the previous stream to drain.
+ *  - Host-side metadata changes when the call returns; device work is
+ *    enqueued on `stream` and ordered with the caller's other work there.
+ *  - A pool is not thread-safe: one host thread at a time per pool.
+ *  - pool == NULL is rejected first with PKV_ERR_BAD_ARG (negated where the
+ *    function returns an id).
+ *  - All floating-point data is IEEE float32.
+ *
+ * Device layouts.
+ *  - Pool storage: block-major [n_blocks][n_layers][2 (K,V)][n_kv_heads]
+ *    [block_size][head_dim] float32 (pkv_pool_storage_bytes bytes).
+ *  - Q and out rows: [rows, n_heads * head_dim]; head h occupies columns
+ *    [h * head_dim, (h + 1) * head_dim).
+ *  - K_new / V_new rows: [rows, n_kv_heads * head_dim].
+ *  - Batched calls take `seqs[M]`; for n rows per sequence, input row
+ *    r * n + t belongs to token t of sequence seqs[r].
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  0..3 are the four codes of "nx_f32_attn_paged.nx source"
+ * (the NX_F32_AP_* constants); 4..8 name failures the pages do not. */
+#define PKV_OK 0
+#define PKV_ERR_BAD_DIM 1     /* a size <= 0, or head shape != the pool's  */
+#define PKV_ERR_BAD_GQA 2     /* n_heads not a multiple of n_kv_heads      */
+#define PKV_ERR_SEQ 3         /* bad/absent/duplicate sequence id, or rows
+                                 not ensured / target block shared         */
+#define PKV_ERR_OOM 4         /* not enough free blocks                     */
+#define PKV_ERR_CAPACITY 5    /* beyond a sequence's max_tokens, or no
+                                 free sequence id                           */
+#define PKV_ERR_BAD_ARG 6     /* other bad argument (layer range, truncate
+                                 length, unknown block, buffer too small,
+                                 NULL pointer, metadata-only pool)          */
+#define PKV_ERR_DEVICE 7      /* a HIP runtime call failed                  */
+#define PKV_ERR_UNSUPPORTED 8 /* shape outside what the kernels handle      */
+
+typedef struct pkv_pool pkv_pool;
+
+/* Human-readable name of a status code (static string). */
+const char *pkv_strerror(int32_t code);
+
+/* ------------------------------------------------------------------------ */
+/* Pool and blocks                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device storage a pool of this shape needs (0 on bad sizes).
+ * ("nx_paged_kv_gate.nx source": nx_pkv_pool_new(n_blocks, n_layers, kv_dim);
+ * the block size, hidden there, is an explicit parameter here.) */
+size_t pkv_pool_storage_bytes(int32_t n_blocks, int32_t block_size,
+                              int32_t n_layers, int32_t n_kv_heads,
+                              int32_t head_dim);
+
+/* Create a pool.  storage_dev (>= pkv_pool_storage_bytes bytes, 256-byte
+ * aligned) is borrowed, never freed; the caller keeps it alive until
+ * pkv_pool_free.  storage_dev == NULL makes a metadata-only pool: every
+ * block, sequence and page-table call works and no device work is ever
+ * done; pkv_append_layer runs its checks and then does nothing, and the
+ * attention calls return PKV_ERR_BAD_ARG.  max_seqs bounds the
+ * number of live sequence ids.  Returns NULL on bad sizes or a HIP failure.
+ * A fresh pool hands out block ids 0, 1, 2, ... in that order. */
+pkv_pool *pkv_pool_new(int32_t n_blocks, int32_t block_size, int32_t n_layers,
+                       int32_t n_kv_heads, int32_t head_dim, int32_t max_seqs,
+                       void *storage_dev, size_t storage_bytes);
+
+/* Wait for the pool's device work, then free its host metadata and the
+ * small device/pinned buffers the library allocated for it. */
+void pkv_pool_free(pkv_pool *pool);
+
+/* Take a free block with one reference; -1 when none is free.
+ * ("nx_paged_kv_gate.nx source", KAT part: ids 0,1,2 then -1 on a pool of 3;
+ * a released id is handed out again.) */
+int64_t pkv_alloc_block(pkv_pool *pool);
+
+/* Drop one reference; at zero the id returns to the free stack, from which
+ * the most recently released id is taken first.  PKV_ERR_BAD_ARG for an id
+ * out of range or already free. */
+int32_t pkv_unref_block(pkv_pool *pool, int64_t id);
+
+/* Placement control: afterwards, allocations return ids[0], ids[1], ... in
+ * that order.  ids[0..n) must be a permutation of exactly the currently free
+ * ids (PKV_ERR_BAD_ARG otherwise).  Used to scatter sequences across the
+ * pool with a seeded permutation. */
+int32_t pkv_pool_set_free_order(pkv_pool *pool, const int64_t *ids,
+                                int32_t n);
+
+/* ------------------------------------------------------------------------ */
+/* Sequences                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* New empty sequence that may hold up to max_tokens rows; returns the lowest
+ * unused id, -PKV_ERR_BAD_ARG for max_tokens <= 0, -PKV_ERR_CAPACITY when
+ * max_seqs ids are live.  ("nx_paged_kv_gate.nx source": nx_pkv_seq_new.) */
+int32_t pkv_seq_new(pkv_pool *pool, int32_t max_tokens);
+
+/* Release every page of the sequence (last page first) and retire its id. */
+int32_t pkv_seq_free(pkv_pool *pool, int32_t seq);
+
+/* New sequence sharing the first ceil(seq_len / block_size) pages of `seq`;
+ * each shared block gains one reference.  Returns the new id or a negated
+ * code.  ("nx_paged_kv_gate.nx source", FORK part: the shared first block
+ * has reference count 2.) */
+int32_t pkv_seq_fork(pkv_pool *pool, int32_t seq);
+
+/* Rewind to new_len rows (0 <= new_len <= seq_len, else PKV_ERR_BAD_ARG):
+ * pages past ceil(new_len / block_size) are released, last page first.
+ * ("nx_paged_kv_gate.nx source": header "truncate unref" and REWIND part.) */
+int32_t pkv_seq_truncate(pkv_pool *pool, int32_t seq, int32_t new_len);
+
+/* ------------------------------------------------------------------------ */
+/* Step protocol                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Reserve room for n_new rows in every sequence of seqs[0..M) and make every
+ * block those rows will land in private.  Per sequence, in batch order:
+ * each existing page in [seq_len / B, ceil((seq_len + n_new) / B)) whose
+ * block is shared is replaced by a fresh copy (ascending page order; the
+ * copy is enqueued on `stream`), then fresh pages are added until
+ * ceil((seq_len + n_new) / B) exist.  The ids this takes over the whole
+ * batch are counted first; if fewer are free, PKV_ERR_OOM and nothing
+ * changes.  Errors: BAD_DIM (M or n_new <= 0), SEQ (bad or repeated id),
+ * CAPACITY (seq_len + n_new > max_tokens), OOM.
+ * ("nx_f32_attn_paged.nx source", caller contract; "nx_f32_llama_v4b.nx
+ * source", the capacity + copy-on-write loop before the layers.) */
+int32_t pkv_ensure_append(pkv_pool *pool, const int32_t *seqs, int32_t M,
+                          int32_t n_new, void *stream);
+
+/* Write K_new_dev / V_new_dev rows [M * n_new, n_kv_heads * head_dim] at
+ * positions seq_len .. seq_len + n_new - 1 of `layer` for each sequence
+ * (one coalesced scatter kernel).  Errors, in this order: BAD_DIM (M or
+ * n_new <= 0), SEQ (bad or repeated id), BAD_ARG (layer out of range), SEQ
+ * (rows not ensured, or a target block shared), BAD_ARG (NULL pointer).
+ * ("nx_f32_attn_paged.nx source": nx_pkv_append_layer in
+ * nx_f32_attn_with_paged, step 1.) */
+int32_t pkv_append_layer(pkv_pool *pool, const int32_t *seqs, int32_t M,
+                         int32_t n_new, int32_t layer, const float *K_new_dev,
+                         const float *V_new_dev, void *stream);
+
+/* seq_len += n for every sequence, once per step after all layers.
+ * Errors: BAD_DIM, SEQ (bad id, or beyond the ensured pages), CAPACITY.
+ * ("nx_f32_llama_v4b.nx source": nx_pkv_advance after the layer loop.) */
+int32_t pkv_advance(pkv_pool *pool, const int32_t *seqs, int32_t M,
+                    int32_t n);
+
+/* ------------------------------------------------------------------------ */
+/* Attention                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Device workspace bytes pkv_attn_paged_decode needs for this batch (split
+ * partial results); depends only on each sequence's length and n_heads.
+ * Returns 0 if no workspace is needed, (size_t)-1 on bad arguments. */
+size_t pkv_decode_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
+                                  int32_t M, int32_t n_heads);
+
+/* Batched decode: one new query row per sequence, already appended with
+ * pkv_append_layer and not yet advanced, so total_k = seq_len + 1 and every
+ * key is visible.  Q_dev, out_dev: [M, n_heads * head_dim], row r for
+ * seqs[r].  Long contexts are split into fixed 512-row key ranges whose
+ * partial softmax states are merged in a fixed order, so each output depends
+ * only on its own sequence (independent of M, batch order and placement).
+ * ws_dev: >= pkv_decode_workspace_bytes bytes (may be NULL when that is 0).
+ * Errors in the pages' order: BAD_DIM (M, n_heads, n_kv_heads, head_dim
+ * <= 0, or head shape != the pool's), BAD_GQA, SEQ, then BAD_ARG (layer,
+ * NULL pointer, workspace too small, metadata-only pool), UNSUPPORTED.
+ * ("nx_f32_llama_v4b.nx source": per-row nx_f32_attn_with_paged with n_q = 1
+ * and causal = 1; "nx_f32_attn_paged.nx source": the attention body.) */
+int32_t pkv_attn_paged_decode(pkv_pool *pool, const int32_t *seqs, int32_t M,
+                              int32_t layer, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t head_dim,
+                              const float *Q_dev, float scale, float *out_dev,
+                              void *ws_dev, size_t ws_bytes, void *stream);
+
+/* Chunked prefill: n_q new rows per sequence (appended, not advanced),
+ * total_k = seq_len + n_q; with causal != 0 query i sees keys
+ * 0 .. total_k - n_q + i, otherwise all total_k keys.  Q_dev, out_dev:
+ * [M * n_q, n_heads * head_dim], row r * n_q + i for query i of seqs[r].
+ * Errors as pkv_attn_paged_decode plus BAD_DIM for n_q <= 0.
+ * ("nx_f32_attn_paged.nx source": header comment, offset-causal rule, and
+ * nx_f32_attn_with_paged.) */
+int32_t pkv_attn_paged_prefill(pkv_pool *pool, const int32_t *seqs,
+                               int32_t M, int32_t n_q, int32_t layer,
+                               int32_t n_heads, int32_t n_kv_heads,
+                               int32_t head_dim, const float *Q_dev,
+                               int32_t causal, float scale, float *out_dev,
+                               void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Contiguous twin (the same kernels reading a contiguous cache)             */
+/*                                                                            */
+/* "nx_f32_attn_paged.nx source" (header comment) and "nx_paged_kv_gate.nx   */
+/* source" (EQUIV part) define the paged path as the contiguous path with    */
+/* only the row storage changed, and require the two to agree bit for bit.   */
+/* These entry points run the same kernels with a contiguous address map,    */
+/* so that agreement can be checked on the GPU.                              */
+/* ------------------------------------------------------------------------ */
+
+/* A contiguous cache of n_slots sequences: device layout
+ * [n_slots][n_layers][2 (K,V)][n_kv_heads][max_seq][head_dim] float32. */
+typedef struct pkv_contig {
+    void *base_dev;
+    int32_t n_slots;
+    int32_t n_layers;
+    int32_t n_kv_heads;
+    int32_t max_seq;
+    int32_t head_dim;
+    int32_t block_size; /* rows per page the kernels iterate by: give the
+                           paged pool's block size to get identical bits */
+} pkv_contig;
+
+/* Bytes of the contiguous cache above (0 on bad sizes). */
+size_t pkv_contig_bytes(int32_t n_slots, int32_t n_layers, int32_t n_kv_heads,
+                        int32_t max_seq, int32_t head_dim);
+
+/* Write rows [M * n_new, kv_dim] of slot slots[r] at positions
+ * seq_lens[r] .. seq_lens[r] + n_new - 1 of `layer`.  seq_lens, slots: host
+ * arrays of M entries. */
+int32_t pkv_contig_append(const pkv_contig *cache, const int32_t *slots,
+                          const int32_t *seq_lens, int32_t M, int32_t n_new,
+                          int32_t layer, const float *K_new_dev,
+                          const float *V_new_dev, void *stream);
+
+/* Workspace for pkv_attn_contig_decode given per-row seq_lens. */
+size_t pkv_contig_decode_workspace_bytes(const int32_t *seq_lens, int32_t M,
+                                         int32_t n_heads, int32_t n_kv_heads,
+                                         int32_t head_dim);
+
+/* As pkv_attn_paged_decode with total_k = seq_lens[r] + 1 over slot
+ * slots[r].  Bit-identical to the paged call on the same rows. */
+int32_t pkv_attn_contig_decode(const pkv_contig *cache, const int32_t *slots,
+                               const int32_t *seq_lens, int32_t M,
+                               int32_t layer, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim,
+                               const float *Q_dev, float scale, float *out_dev,
+                               void *ws_dev, size_t ws_bytes, void *stream);
+
+/* As pkv_attn_paged_prefill with total_k = seq_lens[r] + n_q over slot
+ * slots[r].  Bit-identical to the paged call on the same rows. */
+int32_t pkv_attn_contig_prefill(const pkv_contig *cache, const int32_t *slots,
+                                const int32_t *seq_lens, int32_t M,
+                                int32_t n_q, int32_t layer, int32_t n_heads,
+                                int32_t n_kv_heads, int32_t head_dim,
+                                const float *Q_dev, int32_t causal,
+                                float scale, float *out_dev, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Introspection (bitwise state comparisons)                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Current length of a sequence, or -PKV_ERR_SEQ. */
+int32_t pkv_seq_len(pkv_pool *pool, int32_t seq);
+
+/* Copies up to cap block ids of the page table; returns the page count
+ * (which may exceed cap) or -PKV_ERR_SEQ. */
+int32_t pkv_seq_pages(pkv_pool *pool, int32_t seq, int64_t *out, int32_t cap);
+
+/* Copies the n_blocks reference counts; returns n_blocks. */
+int32_t pkv_pool_refcounts(pkv_pool *pool, int32_t *out);
+
+/* Copies up to cap free ids from the bottom of the free stack to its top
+ * (the last one is taken next); returns the number of free ids. */
+int32_t pkv_pool_free_stack(pkv_pool *pool, int64_t *out, int32_t cap);
+
+/* ------------------------------------------------------------------------ */
+/* Kernel timing                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Kernel ids for pkv_profile_read. */
+#define PKV_K_APPEND 0
+#define PKV_K_DECODE 1   /* the split decode kernel */
+#define PKV_K_COMBINE 2  /* the split-merge kernel */
+#define PKV_K_PREFILL 3
+#define PKV_K_COW 4
+#define PKV_K_COUNT 5
+
+/* on != 0: record a HIP event pair on the launch stream around every kernel
+ * the pool launches; on == 0: stop.  Either way, clears the totals. */
+int32_t pkv_profile_enable(pkv_pool *pool, int32_t on);
+
+/* Wait for the recorded events and report the summed kernel time (ms) and
+ * launch count of one kernel id since profiling was enabled. */
+int32_t pkv_profile_read(pkv_pool *pool, int32_t kernel, double *total_ms,
+                         int64_t *launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

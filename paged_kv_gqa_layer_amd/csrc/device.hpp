@@ -1,0 +1,126 @@
+// Descriptors shared by the host launch code and the gfx950 kernels, plus the
+// host-side launcher declarations.
+//
+// A call's batch is described by one int32 blob uploaded per call:
+//   RowDesc[M]  per sequence row: total_k, page-list offset, split count...
+//   Item[W]     per work item (sequence row, query, key split)
+//   OutDesc[Mo] per output row: first item and split count (split merge)
+//   pages[]     the batch's page tables, concatenated (block ids)
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pkv {
+
+struct RowDesc {
+  int32_t total_k;  // keys this row attends over (append: first position)
+  int32_t pt_off;   // paged: offset of the row's page ids; contiguous: slot
+  int32_t n_pages;  // page ids present for this row
+  int32_t pad;
+};
+
+struct Item {
+  int32_t row;    // sequence row
+  int32_t qi;     // query within the row (0 for decode)
+  int32_t split;  // key split index
+  int32_t nsp;    // number of splits of this (row, query)
+};
+
+struct OutDesc {
+  int32_t first_item;
+  int32_t n_splits;
+};
+
+// Address of one page (block_size consecutive positions) of one kv head:
+// K rows at the returned pointer, V rows at + v_off; position t of the page
+// at + t * head_dim.
+struct PagedMap {
+  float* base;
+  const int32_t* pages;
+  int64_t block_stride;  // floats per block (all layers)
+  int64_t layer_off;     // floats from block start to this layer
+  int64_t head_stride;   // floats between kv heads
+  int64_t v_off;         // floats from the K part to the V part
+  int32_t block_size;
+  __device__ __forceinline__ float* page(const RowDesc& rd, int32_t p,
+                                         int32_t kvh) const {
+    const int64_t b = pages[rd.pt_off + p];
+    return base + b * block_stride + layer_off + kvh * head_stride;
+  }
+};
+
+struct ContigMap {
+  float* base;
+  int64_t slot_stride;  // floats per sequence slot (all layers)
+  int64_t layer_off;
+  int64_t head_stride;  // max_seq * head_dim
+  int64_t v_off;        // n_kv_heads * max_seq * head_dim
+  int64_t page_stride;  // block_size * head_dim
+  int32_t block_size;
+  __device__ __forceinline__ float* page(const RowDesc& rd, int32_t p,
+                                         int32_t kvh) const {
+    return base + rd.pt_off * slot_stride + layer_off + kvh * head_stride +
+           p * page_stride;
+  }
+};
+
+// Key positions per split of the specialised decode kernel (a multiple of
+// its 16-row page).
+constexpr int32_t kDecodeSplit = 512;
+// Queries per workgroup of the MFMA prefill kernel.
+constexpr int32_t kPrefillQTile = 32;
+
+// Kernel shapes the specialised paths cover.
+inline bool fast_decode_ok(int32_t head_dim, int32_t group, int32_t block) {
+  return head_dim == 128 && block == 16 &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
+}
+inline bool fast_prefill_ok(int32_t head_dim, int32_t group, int32_t block) {
+  return head_dim == 128 && block == 16 && group == 4;
+}
+
+struct AttnArgs {
+  const RowDesc* rows;
+  const Item* items;
+  const OutDesc* outs;
+  const float* Q;
+  float* out;
+  float* part_o;   // [items][n_heads][head_dim]
+  float* part_ml;  // [items][n_heads][2]
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t n_q;
+  int32_t causal;
+  float qscale;  // scale * log2(e): scores are kept in base-2 units
+  int32_t n_items;
+  int32_t n_outs;
+  int32_t split;  // generic kernel: key positions per split item
+};
+
+// Launchers (kernels.hip).  Each returns hipSuccess or the launch error.
+hipError_t launch_append(const PagedMap& m, const RowDesc* rows,
+                         const float* K, const float* V, int32_t M, int32_t n,
+                         int32_t kv_dim, int32_t head_dim, hipStream_t st);
+hipError_t launch_append(const ContigMap& m, const RowDesc* rows,
+                         const float* K, const float* V, int32_t M, int32_t n,
+                         int32_t kv_dim, int32_t head_dim, hipStream_t st);
+hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,
+                      int64_t block_floats, hipStream_t st);
+hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st);
+hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st);
+hipError_t launch_generic(const PagedMap& m, const AttnArgs& a,
+                          int32_t group, hipStream_t st);
+hipError_t launch_generic(const ContigMap& m, const AttnArgs& a,
+                          int32_t group, hipStream_t st);
+hipError_t launch_combine(const AttnArgs& a, hipStream_t st);
+hipError_t launch_prefill_mfma(const PagedMap& m, const AttnArgs& a,
+                               int32_t M, hipStream_t st);
+hipError_t launch_prefill_mfma(const ContigMap& m, const AttnArgs& a,
+                               int32_t M, hipStream_t st);
+
+}  // namespace pkv

@@ -1,0 +1,799 @@
+// gfx950 (CDNA4) kernels for paged-KV grouped-query attention.
+//
+// What is computed ("nx_f32_attn_paged.nx source", header comment and
+// nx_f32_attn_with_paged; "nx_f32_gqa_attention.nx source", header):
+// query head h reads kv head h / group; query i of a row sits at position
+// total_k - n_q + i and (causal) sees keys 0..that position; the output is
+// softmax(q K^T * scale) V written at columns [h*head_dim, (h+1)*head_dim) of
+// the query's output row.
+//
+// Every kernel is a template over the K/V address map (PagedMap: through the
+// page table; ContigMap: a contiguous cache).  The arithmetic does not depend
+// on the map, so the paged and contiguous forms are bit-identical.
+//
+// Scores are kept in base-2 units: q is prescaled by scale*log2(e) and the
+// softmax uses exp2; the split merge uses the same units.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+
+namespace pkv {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+// DPP row (16-lane) permutations.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                         0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the same
+// bits (each stage adds a lane's value to its partner's, and IEEE addition
+// commutes).  Pairings: xor 1, xor 2, mirror within 8 lanes, rotate by 8.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x128>(v);  // row_ror:8
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float4 ld4(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+
+__device__ __forceinline__ float dot8(const float4& ka, const float4& kb,
+                                      const float (&qa)[4],
+                                      const float (&qb)[4]) {
+  float s = ka.x * qa[0];
+  s = fmaf(ka.y, qa[1], s);
+  s = fmaf(ka.z, qa[2], s);
+  s = fmaf(ka.w, qa[3], s);
+  s = fmaf(kb.x, qb[0], s);
+  s = fmaf(kb.y, qb[1], s);
+  s = fmaf(kb.z, qb[2], s);
+  s = fmaf(kb.w, qb[3], s);
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Append: scatter new K/V rows to their (page, slot).  One thread per VEC
+// floats; a row of one kv head is head_dim contiguous floats on both sides.
+// ---------------------------------------------------------------------------
+template <int VEC, class Map>
+__global__ __launch_bounds__(256) void append_kernel(
+    Map m, const RowDesc* __restrict__ rows, const float* __restrict__ K,
+    const float* __restrict__ V, int32_t n, int32_t kv_dim, int32_t head_dim,
+    int64_t total) {
+  const int32_t per_row = kv_dim / VEC;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t rt = e / per_row;
+    const int32_t c = static_cast<int32_t>(e - rt * per_row) * VEC;
+    const int32_t r = static_cast<int32_t>(rt / n);
+    const int32_t t = static_cast<int32_t>(rt - (int64_t)r * n);
+    const RowDesc rd = rows[r];
+    const int32_t pos = rd.total_k + t;
+    const int32_t kvh = c / head_dim;
+    const int32_t d = c - kvh * head_dim;
+    float* dst = m.page(rd, pos / m.block_size, kvh) +
+                 (int64_t)(pos % m.block_size) * head_dim + d;
+    const int64_t src = rt * kv_dim + c;
+    if constexpr (VEC == 4) {
+      *reinterpret_cast<float4*>(dst) = ld4(K + src);
+      *reinterpret_cast<float4*>(dst + m.v_off) = ld4(V + src);
+    } else {
+      dst[0] = K[src];
+      dst[m.v_off] = V[src];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Copy-on-append: copy whole blocks (all layers, K and V) src -> dst.
+// ---------------------------------------------------------------------------
+template <int VEC>
+__global__ __launch_bounds__(256) void cow_kernel(float* base,
+                                                  const int32_t* __restrict__ pairs,
+                                                  int64_t block_floats) {
+  const int64_t src = pairs[2 * blockIdx.y];
+  const int64_t dst = pairs[2 * blockIdx.y + 1];
+  const float* s = base + src * block_floats;
+  float* d = base + dst * block_floats;
+  const int64_t n = block_floats / VEC;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    if constexpr (VEC == 4) {
+      reinterpret_cast<float4*>(d)[e] = reinterpret_cast<const float4*>(s)[e];
+    } else {
+      d[e] = s[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode, head_dim 128, 16-row pages: one 64-lane wave per
+// (work item = row x 512-key split, kv head).
+//
+// Lane layout: lane = 16 * rr + c.  For each page the wave reads the kv
+// head's 16 x 128 K tile and V tile once, four positions per load step:
+// position 4*i + rr, dims [4c, 4c+4) and [64+4c, 64+4c+4).  Each K/V byte
+// is loaded once and used for all GROUP query heads of the kv head (the GQA
+// sharing).  Partial dot products are summed over the 16 lanes of a DPP row
+// (row16_sum), so every lane of row rr holds the full scores of positions
+// 4*i + rr for all GROUP heads.  Each row keeps its own online-softmax state
+// (m, l, o) over the positions it sees; the four row states are merged at
+// the end of the split with cross-row shuffles.
+// ---------------------------------------------------------------------------
+template <int GROUP, class Map>
+__global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
+  constexpr int D = 128;
+  constexpr int B = 16;
+  constexpr int NI = B / 4;
+  const int32_t G = a.n_kv_heads;
+  const int32_t item_idx = blockIdx.x / G;
+  const int32_t kvh = blockIdx.x - item_idx * G;
+  const Item it = a.items[item_idx];
+  const RowDesc rd = a.rows[it.row];
+  const int lane = threadIdx.x;
+  const int rr = lane >> 4;
+  const int c = lane & 15;
+
+  const int32_t total_k = rd.total_k;
+  const int32_t k_begin = it.split * kDecodeSplit;
+  const int32_t k_end = min(total_k, k_begin + kDecodeSplit);
+  const int32_t p_begin = k_begin / B;
+  const int32_t p_end = (k_end + B - 1) / B;
+
+  float qa[GROUP][4], qb[GROUP][4];
+  {
+    const float* qrow =
+        a.Q + ((int64_t)it.row * a.n_heads + (int64_t)kvh * GROUP) * D;
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      const float4 x = ld4(qrow + j * D + 4 * c);
+      const float4 y = ld4(qrow + j * D + 64 + 4 * c);
+      qa[j][0] = x.x * a.qscale;
+      qa[j][1] = x.y * a.qscale;
+      qa[j][2] = x.z * a.qscale;
+      qa[j][3] = x.w * a.qscale;
+      qb[j][0] = y.x * a.qscale;
+      qb[j][1] = y.y * a.qscale;
+      qb[j][2] = y.z * a.qscale;
+      qb[j][3] = y.w * a.qscale;
+    }
+  }
+
+  float mrun[GROUP], lrun[GROUP];
+  float oa[GROUP][4], ob[GROUP][4];
+#pragma unroll
+  for (int j = 0; j < GROUP; ++j) {
+    mrun[j] = kNegInf;
+    lrun[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) oa[j][e] = ob[j][e] = 0.f;
+  }
+
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+  float4 kA[NI], kB[NI], vA[NI], vB[NI];
+  auto load_page = [&](int32_t p, float4(&ka)[NI], float4(&kb)[NI],
+                       float4(&va)[NI], float4(&vb)[NI]) {
+    const float* kp = m.page(rd, p, kvh);
+    const float* vp = kp + m.v_off;
+    const int32_t n_valid = min(B, k_end - p * B);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int t = 4 * i + rr;
+      const int off = t * D + 4 * c;
+      if (t < n_valid) {
+        ka[i] = ld4(kp + off);
+        kb[i] = ld4(kp + off + 64);
+        va[i] = ld4(vp + off);
+        vb[i] = ld4(vp + off + 64);
+      } else {
+        ka[i] = kb[i] = va[i] = vb[i] = zero4;
+      }
+    }
+  };
+
+  load_page(p_begin, kA, kB, vA, vB);
+  for (int32_t p = p_begin; p < p_end; ++p) {
+    float4 nkA[NI], nkB[NI], nvA[NI], nvB[NI];
+    if (p + 1 < p_end) load_page(p + 1, nkA, nkB, nvA, nvB);
+
+    const int32_t n_valid = min(B, k_end - p * B);
+    float s[NI][GROUP];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+#pragma unroll
+      for (int j = 0; j < GROUP; ++j)
+        s[i][j] = row16_sum(dot8(kA[i], kB[i], qa[j], qb[j]));
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (4 * i + rr >= n_valid) {
+#pragma unroll
+        for (int j = 0; j < GROUP; ++j) s[i][j] = kNegInf;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      float mx = s[0][j];
+#pragma unroll
+      for (int i = 1; i < NI; ++i) mx = fmaxf(mx, s[i][j]);
+      const float m_new = fmaxf(mrun[j], mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(mrun[j] - m_use);
+      float pr[NI];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        pr[i] = fast_exp2(s[i][j] - m_use);
+        psum += pr[i];
+      }
+      lrun[j] = fmaf(lrun[j], alpha, psum);
+      mrun[j] = m_new;
+      float xa[4], xb[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xa[e] = oa[j][e] * alpha;
+        xb[e] = ob[j][e] * alpha;
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        xa[0] = fmaf(pr[i], vA[i].x, xa[0]);
+        xa[1] = fmaf(pr[i], vA[i].y, xa[1]);
+        xa[2] = fmaf(pr[i], vA[i].z, xa[2]);
+        xa[3] = fmaf(pr[i], vA[i].w, xa[3]);
+        xb[0] = fmaf(pr[i], vB[i].x, xb[0]);
+        xb[1] = fmaf(pr[i], vB[i].y, xb[1]);
+        xb[2] = fmaf(pr[i], vB[i].z, xb[2]);
+        xb[3] = fmaf(pr[i], vB[i].w, xb[3]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        oa[j][e] = xa[e];
+        ob[j][e] = xb[e];
+      }
+    }
+
+    if (p + 1 < p_end) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        kA[i] = nkA[i];
+        kB[i] = nkB[i];
+        vA[i] = nvA[i];
+        vB[i] = nvB[i];
+      }
+    }
+  }
+
+  // Merge the four row states (lanes 16 and 32 apart hold the other rows).
+  float Lf[GROUP];
+#pragma unroll
+  for (int j = 0; j < GROUP; ++j) {
+    float M = fmaxf(mrun[j], __shfl_xor(mrun[j], 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    // every split holds at least one key, so M is finite
+    const float w = fast_exp2(mrun[j] - M);
+    float L = lrun[j] * w;
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    Lf[j] = L;
+    mrun[j] = M;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x = oa[j][e] * w;
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      oa[j][e] = x;
+      float y = ob[j][e] * w;
+      y += __shfl_xor(y, 16);
+      y += __shfl_xor(y, 32);
+      ob[j][e] = y;
+    }
+  }
+
+  // Row rr writes heads j with j % 4 == rr.
+  if (it.nsp == 1) {
+    float* orow = a.out + ((int64_t)it.row * a.n_heads + (int64_t)kvh * GROUP) * D;
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      if ((j & 3) == rr) {
+        float4 x, y;
+        x.x = oa[j][0] / Lf[j];
+        x.y = oa[j][1] / Lf[j];
+        x.z = oa[j][2] / Lf[j];
+        x.w = oa[j][3] / Lf[j];
+        y.x = ob[j][0] / Lf[j];
+        y.y = ob[j][1] / Lf[j];
+        y.z = ob[j][2] / Lf[j];
+        y.w = ob[j][3] / Lf[j];
+        *reinterpret_cast<float4*>(orow + j * D + 4 * c) = x;
+        *reinterpret_cast<float4*>(orow + j * D + 64 + 4 * c) = y;
+      }
+    }
+  } else {
+    const int64_t hbase = (int64_t)item_idx * a.n_heads + (int64_t)kvh * GROUP;
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j) {
+      if ((j & 3) == rr) {
+        float* po = a.part_o + (hbase + j) * D;
+        *reinterpret_cast<float4*>(po + 4 * c) =
+            make_float4(oa[j][0], oa[j][1], oa[j][2], oa[j][3]);
+        *reinterpret_cast<float4*>(po + 64 + 4 * c) =
+            make_float4(ob[j][0], ob[j][1], ob[j][2], ob[j][3]);
+        if (c == 0) {
+          a.part_ml[(hbase + j) * 2 + 0] = mrun[j];
+          a.part_ml[(hbase + j) * 2 + 1] = Lf[j];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic attention (any head_dim, group, page size; decode or prefill): one
+// wave per (work item = row x query x key split, kv head).  Lanes take 64
+// keys at a time for the scores; for the weighted sum they take dims.
+// ---------------------------------------------------------------------------
+constexpr int kGenericMaxGroup = 16;
+
+template <class Map>
+__global__ __launch_bounds__(64) void generic_kernel(Map m, AttnArgs a,
+                                                     int32_t group) {
+  extern __shared__ float sh[];
+  const int32_t D = a.head_dim;
+  const int32_t G = a.n_kv_heads;
+  const int32_t item_idx = blockIdx.x / G;
+  const int32_t kvh = blockIdx.x - item_idx * G;
+  const Item it = a.items[item_idx];
+  const RowDesc rd = a.rows[it.row];
+  const int lane = threadIdx.x;
+  float* q_sh = sh;                // [group][D]
+  float* o_sh = q_sh + group * D;  // [group][D]
+  float* p_sh = o_sh + group * D;  // [group][64]
+
+  const int32_t total_k = rd.total_k;
+  const int32_t q_pos = total_k - a.n_q + it.qi;
+  const int32_t vis = a.causal ? q_pos + 1 : total_k;
+  const int32_t k_begin = it.split * a.split;
+  const int32_t k_end = min(vis, k_begin + a.split);
+  const int64_t out_row = (int64_t)it.row * a.n_q + it.qi;
+
+  const float* qrow = a.Q + (out_row * a.n_heads + (int64_t)kvh * group) * D;
+  for (int32_t e = lane; e < group * D; e += 64) {
+    q_sh[e] = qrow[e] * a.qscale;
+    o_sh[e] = 0.f;
+  }
+  __syncthreads();
+
+  float mrun[kGenericMaxGroup], lrun[kGenericMaxGroup], alpha[kGenericMaxGroup];
+#pragma unroll
+  for (int j = 0; j < kGenericMaxGroup; ++j) {
+    mrun[j] = kNegInf;
+    lrun[j] = 0.f;
+    alpha[j] = 1.f;
+  }
+
+  const int32_t B = m.block_size;
+  for (int32_t c0 = k_begin; c0 < k_end; c0 += 64) {
+    const int32_t key = c0 + lane;
+    const bool valid = key < k_end;
+    const float* kr = valid ? m.page(rd, key / B, kvh) + (int64_t)(key % B) * D
+                            : nullptr;
+#pragma unroll
+    for (int j = 0; j < kGenericMaxGroup; ++j) {
+      if (j < group) {
+        float s = kNegInf;
+        if (valid) {
+          float acc = 0.f;
+          for (int32_t d = 0; d < D; ++d) acc = fmaf(q_sh[j * D + d], kr[d], acc);
+          s = acc;
+        }
+        const float m_new = fmaxf(mrun[j], wave_max(s));
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float p = valid ? fast_exp2(s - m_use) : 0.f;
+        alpha[j] = fast_exp2(mrun[j] - m_use);
+        lrun[j] = fmaf(lrun[j], alpha[j], wave_sum(p));
+        mrun[j] = m_new;
+        p_sh[j * 64 + lane] = p;
+      }
+    }
+    __syncthreads();
+    const int32_t n_here = min(64, k_end - c0);
+    for (int32_t d = lane; d < D; d += 64) {
+#pragma unroll
+      for (int j = 0; j < kGenericMaxGroup; ++j) {
+        if (j < group) {
+          float acc = o_sh[j * D + d] * alpha[j];
+          for (int32_t k = 0; k < n_here; ++k) {
+            const int32_t kk = c0 + k;
+            const float* vr = m.page(rd, kk / B, kvh) + m.v_off +
+                              (int64_t)(kk % B) * D;
+            acc = fmaf(p_sh[j * 64 + k], vr[d], acc);
+          }
+          o_sh[j * D + d] = acc;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (it.nsp == 1) {
+    float* orow = a.out + (out_row * a.n_heads + (int64_t)kvh * group) * D;
+    for (int32_t d = lane; d < D; d += 64) {
+#pragma unroll
+      for (int j = 0; j < kGenericMaxGroup; ++j)
+        if (j < group) orow[j * D + d] = o_sh[j * D + d] / lrun[j];
+    }
+  } else {
+    const int64_t hbase = (int64_t)item_idx * a.n_heads + (int64_t)kvh * group;
+    for (int32_t d = lane; d < D; d += 64) {
+#pragma unroll
+      for (int j = 0; j < kGenericMaxGroup; ++j)
+        if (j < group) a.part_o[(hbase + j) * D + d] = o_sh[j * D + d];
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < kGenericMaxGroup; ++j) {
+        if (j < group) {
+          a.part_ml[(hbase + j) * 2 + 0] = mrun[j];
+          a.part_ml[(hbase + j) * 2 + 1] = lrun[j];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split merge: out = sum_s w_s o_s / sum_s w_s l_s, w_s = 2^(m_s - max m),
+// in ascending split order (fixed, so results do not depend on scheduling).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
+  const int32_t h = blockIdx.x;
+  const int32_t o = blockIdx.y;
+  const OutDesc od = a.outs[o];
+  if (od.n_splits <= 1) return;
+  const int32_t D = a.head_dim;
+  const float* ml = a.part_ml;
+  float M = kNegInf;
+  for (int32_t s = 0; s < od.n_splits; ++s)
+    M = fmaxf(M, ml[((int64_t)(od.first_item + s) * a.n_heads + h) * 2]);
+  float L = 0.f;
+  for (int32_t s = 0; s < od.n_splits; ++s) {
+    const int64_t i = ((int64_t)(od.first_item + s) * a.n_heads + h) * 2;
+    L = fmaf(ml[i + 1], fast_exp2(ml[i] - M), L);
+  }
+  for (int32_t d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.f;
+    for (int32_t s = 0; s < od.n_splits; ++s) {
+      const int64_t hi = (int64_t)(od.first_item + s) * a.n_heads + h;
+      acc = fmaf(a.part_o[hi * D + d], fast_exp2(ml[hi * 2] - M), acc);
+    }
+    a.out[((int64_t)o * a.n_heads + h) * D + d] = acc / L;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunked prefill on FP32 MFMA (v_mfma_f32_32x32x2_f32), head_dim 128, GQA
+// group 4, 16-row pages.
+//
+// Workgroup = 4 waves = 32 queries of one (row, kv head).  Each wave owns 32
+// MFMA rows = 8 queries x the 4 heads of the group (row = 4*query + head), so
+// one K/V tile feeds all four heads.  Keys are processed in tiles of 32 (two
+// pages) staged in LDS by the whole workgroup.
+//
+//   S^T[key][row] = sum_d K[key][d] Q[row][d]     (64 MFMAs, K=2 each)
+//   mask (offset-causal), online softmax per row
+//   O[row][d]   += sum_key P[row][key] V[key][d]  (4 x 16 MFMAs)
+//
+// 32x32 MFMA operand/result layout: lane l supplies A[l%32][l/32] and
+// B[l/32][l%32]; accumulator r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
+// Computing S transposed leaves each lane with one row's scores, so the
+// softmax statistics are lane-local; the contraction index of the PV
+// product is permuted to match (key 8*(s/4) + 4*h + s%4 at step s).
+// ---------------------------------------------------------------------------
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+template <class Map>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(Map m, AttnArgs a,
+                                                          int32_t n_qt,
+                                                          int32_t n_wg) {
+  constexpr int D = 128;
+  constexpr int KT = 32;
+  constexpr int KSTR = 132;  // padded LDS row strides (bank spread)
+  constexpr int VSTR = 136;
+  __shared__ float Ks[KT * KSTR];
+  __shared__ float Vs[KT * VSTR];
+
+  // Keep all query tiles of one (row, kv head) on one XCD (they share K/V).
+  const int32_t b = blockIdx.x;
+  const int32_t Lw = (n_wg % 8 == 0) ? (b % 8) * (n_wg / 8) + b / 8 : b;
+  const int32_t G = a.n_kv_heads;
+  const int32_t row = Lw / (G * n_qt);
+  const int32_t rem = Lw - row * G * n_qt;
+  const int32_t kvh = rem / n_qt;
+  const int32_t qt = rem - kvh * n_qt;
+  const RowDesc rd = a.rows[row];
+  const int32_t total_k = rd.total_k;
+  const int32_t n_q = a.n_q;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int h = lane >> 5;
+  const int lr = lane & 31;
+  const int32_t q0 = qt * kPrefillQTile;
+
+  // this lane's MFMA row
+  const int32_t qi = q0 + 8 * w + (lr >> 2);
+  const int32_t jh = lr & 3;
+  const bool row_valid = qi < n_q;
+  const int32_t q_pos = row_valid ? total_k - n_q + qi : total_k - 1;
+
+  float4 qreg[16];
+  {
+    const float* qp = a.Q +
+        (((int64_t)row * n_q + (row_valid ? qi : 0)) * a.n_heads + kvh * 4 + jh) * D +
+        4 * h;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float4 x = row_valid ? ld4(qp + 8 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
+      x.x *= a.qscale;
+      x.y *= a.qscale;
+      x.z *= a.qscale;
+      x.w *= a.qscale;
+      qreg[t] = x;
+    }
+  }
+
+  const int32_t q_last = min(q0 + kPrefillQTile, n_q) - 1;
+  const int32_t kmax = a.causal ? total_k - n_q + q_last + 1 : total_k;
+  const int32_t n_tiles = (kmax + KT - 1) / KT;
+  const int32_t wq_first = q0 + 8 * w;
+  const int32_t wq_last = min(q0 + 8 * w + 7, n_q - 1);
+  const int32_t wkmax = (wq_first > wq_last)
+                            ? 0
+                            : (a.causal ? total_k - n_q + wq_last + 1 : total_k);
+
+  floatx16 O0 = {}, O1 = {}, O2 = {}, O3 = {};
+  float m_run = kNegInf;
+  float l_run = 0.f;
+
+  // tile loader: float4 index tid + 256*u, u < 4: key tid/32 + 8u, dims 4*(tid%32)
+  const int ld_key = tid >> 5;
+  const int ld_c = (tid & 31) * 4;
+  float4 kr[4], vr[4];
+  auto load_tile = [&](int32_t t) {
+    const int32_t k0 = t * KT;
+    const int32_t pg = k0 / 16;
+    const float* p0 = m.page(rd, pg, kvh);
+    const float* p1 = (k0 + 16 < total_k) ? m.page(rd, pg + 1, kvh) : p0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int key = ld_key + 8 * u;
+      const float* base = (u < 2) ? p0 : p1;
+      const int off = (key & 15) * D + ld_c;
+      if (k0 + key < total_k) {
+        kr[u] = ld4(base + off);
+        vr[u] = ld4(base + m.v_off + off);
+      } else {
+        kr[u] = vr[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int key = ld_key + 8 * u;
+      *reinterpret_cast<float4*>(&Ks[key * KSTR + ld_c]) = kr[u];
+      *reinterpret_cast<float4*>(&Vs[key * VSTR + ld_c]) = vr[u];
+    }
+  };
+
+  load_tile(0);
+  store_tile();
+  __syncthreads();
+  for (int32_t t = 0; t < n_tiles; ++t) {
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    const int32_t k0 = t * KT;
+    if (k0 < wkmax) {
+      floatx16 S = {};
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const float4 kf = *reinterpret_cast<const float4*>(&Ks[lr * KSTR + 8 * u + 4 * h]);
+        S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x, qreg[u].x, S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.y, qreg[u].y, S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.z, qreg[u].z, S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qreg[u].w, S, 0, 0, 0);
+      }
+      // mask and row max: this lane holds row lr, keys k0 + 8*(r/4) + 4*h + r%4
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int32_t key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const bool vis = a.causal ? (key <= q_pos) : (key < total_k);
+        if (!vis) S[r] = kNegInf;
+        mx = fmaxf(mx, S[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);  // finite: key 0 is seen in tile 0
+      const float alpha = fast_exp2(m_run - m_new);
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        S[r] = fast_exp2(S[r] - m_new);
+        ps += S[r];
+      }
+      ps += __shfl_xor(ps, 32);
+      l_run = fmaf(l_run, alpha, ps);
+      m_run = m_new;
+      // rescale O: accumulator r holds row 8*(r/4) + 4*h + r%4
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float ar = __shfl(alpha, 8 * (r >> 2) + 4 * h + (r & 3));
+        O0[r] *= ar;
+        O1[r] *= ar;
+        O2[r] *= ar;
+        O3[r] *= ar;
+      }
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const int key = 8 * (s >> 2) + 4 * h + (s & 3);
+        const float* vrow = &Vs[key * VSTR + lr];
+        O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(S[s], vrow[0], O0, 0, 0, 0);
+        O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(S[s], vrow[32], O1, 0, 0, 0);
+        O2 = __builtin_amdgcn_mfma_f32_32x32x2f32(S[s], vrow[64], O2, 0, 0, 0);
+        O3 = __builtin_amdgcn_mfma_f32_32x32x2f32(S[s], vrow[96], O3, 0, 0, 0);
+      }
+    }
+    __syncthreads();
+    if (t + 1 < n_tiles) {
+      store_tile();
+      __syncthreads();
+    }
+  }
+
+  // normalise and store: accumulator r holds row 8*(r/4) + 4*h + r%4, dim 32*db + lr
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rowr = 8 * (r >> 2) + 4 * h + (r & 3);
+    const float lsum = __shfl(l_run, rowr);
+    const int32_t qq = q0 + 8 * w + (rowr >> 2);
+    const int32_t jj = rowr & 3;
+    if (qq < n_q) {
+      float* op = a.out + (((int64_t)row * n_q + qq) * a.n_heads + kvh * 4 + jj) * D + lr;
+      op[0] = O0[r] / lsum;
+      op[32] = O1[r] / lsum;
+      op[64] = O2[r] / lsum;
+      op[96] = O3[r] / lsum;
+    }
+  }
+}
+
+template <class Map>
+hipError_t append_impl(const Map& m, const RowDesc* rows, const float* K,
+                       const float* V, int32_t M, int32_t n, int32_t kv_dim,
+                       int32_t head_dim, hipStream_t st) {
+  const bool vec = (head_dim % 4 == 0);
+  const int64_t total = (int64_t)M * n * kv_dim / (vec ? 4 : 1);
+  const int64_t want = (total + 255) / 256;
+  const int grid = static_cast<int>(want < 65536 ? (want > 0 ? want : 1) : 65536);
+  if (vec)
+    append_kernel<4, Map><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim, head_dim, total);
+  else
+    append_kernel<1, Map><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim, head_dim, total);
+  return hipGetLastError();
+}
+
+template <class Map>
+hipError_t decode_fast_impl(const Map& m, const AttnArgs& a, int32_t group,
+                            hipStream_t st) {
+  const dim3 grid(a.n_items * a.n_kv_heads);
+  switch (group) {
+    case 1: decode_fast_kernel<1, Map><<<grid, 64, 0, st>>>(m, a); break;
+    case 2: decode_fast_kernel<2, Map><<<grid, 64, 0, st>>>(m, a); break;
+    case 4: decode_fast_kernel<4, Map><<<grid, 64, 0, st>>>(m, a); break;
+    case 8: decode_fast_kernel<8, Map><<<grid, 64, 0, st>>>(m, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class Map>
+hipError_t generic_impl(const Map& m, const AttnArgs& a, int32_t group,
+                        hipStream_t st) {
+  if (group > kGenericMaxGroup) return hipErrorInvalidValue;
+  const size_t lds = sizeof(float) * (2 * (size_t)group * a.head_dim + (size_t)group * 64);
+  const dim3 grid(a.n_items * a.n_kv_heads);
+  generic_kernel<Map><<<grid, 64, lds, st>>>(m, a, group);
+  return hipGetLastError();
+}
+
+template <class Map>
+hipError_t prefill_impl(const Map& m, const AttnArgs& a, int32_t M,
+                        hipStream_t st) {
+  const int32_t n_qt = (a.n_q + kPrefillQTile - 1) / kPrefillQTile;
+  const int32_t n_wg = M * a.n_kv_heads * n_qt;
+  prefill_mfma_kernel<Map><<<n_wg, 256, 0, st>>>(m, a, n_qt, n_wg);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const PagedMap& m, const RowDesc* rows, const float* K,
+                         const float* V, int32_t M, int32_t n, int32_t kv_dim,
+                         int32_t head_dim, hipStream_t st) {
+  return append_impl(m, rows, K, V, M, n, kv_dim, head_dim, st);
+}
+hipError_t launch_append(const ContigMap& m, const RowDesc* rows,
+                         const float* K, const float* V, int32_t M, int32_t n,
+                         int32_t kv_dim, int32_t head_dim, hipStream_t st) {
+  return append_impl(m, rows, K, V, M, n, kv_dim, head_dim, st);
+}
+
+hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,
+                      int64_t block_floats, hipStream_t st) {
+  const bool vec = (block_floats % 4 == 0);
+  const int64_t n = block_floats / (vec ? 4 : 1);
+  const int64_t want = (n + 255) / 256;
+  const dim3 grid(static_cast<unsigned>(want < 1024 ? want : 1024), n_pairs);
+  if (vec)
+    cow_kernel<4><<<grid, 256, 0, st>>>(base, pairs, block_floats);
+  else
+    cow_kernel<1><<<grid, 256, 0, st>>>(base, pairs, block_floats);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st) {
+  return decode_fast_impl(m, a, group, st);
+}
+hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st) {
+  return decode_fast_impl(m, a, group, st);
+}
+hipError_t launch_generic(const PagedMap& m, const AttnArgs& a, int32_t group,
+                          hipStream_t st) {
+  return generic_impl(m, a, group, st);
+}
+hipError_t launch_generic(const ContigMap& m, const AttnArgs& a, int32_t group,
+                          hipStream_t st) {
+  return generic_impl(m, a, group, st);
+}
+hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid(a.n_heads, a.n_outs);
+  combine_kernel<<<grid, 128, 0, st>>>(a);
+  return hipGetLastError();
+}
+hipError_t launch_prefill_mfma(const PagedMap& m, const AttnArgs& a, int32_t M,
+                               hipStream_t st) {
+  return prefill_impl(m, a, M, st);
+}
+hipError_t launch_prefill_mfma(const ContigMap& m, const AttnArgs& a,
+                               int32_t M, hipStream_t st) {
+  return prefill_impl(m, a, M, st);
+}
+
+}  // namespace pkv

@@ -1,0 +1,177 @@
+"""The C-ABI library on the CPU: it loads, exports what include/pkv.h
+declares, and its host-side pool logic matches the oracle's state bit for bit
+(reference counts, free stack, page tables, lengths, status codes) on the
+pages' known answers and on seeded random operation sequences.  No kernel is
+launched: the pools here are metadata-only.
+"""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import paged_kv_gqa_layer_amd as pkv
+import synth
+from conftest import ROOT, read_golden
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "pkv.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(pkv_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert len(names) >= 25
+    L = pkv.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(pkv._lib.SIGNATURES), "binding out of date"
+
+
+def test_strerror_and_storage_bytes():
+    L = pkv.lib()
+    assert L.pkv_strerror(0) == b"ok"
+    assert pkv.pool_storage_bytes(10, 16, 2, 8, 128) == 10 * 2 * 2 * 8 * 16 * 128 * 4
+    assert pkv.pool_storage_bytes(0, 16, 2, 8, 128) == 0
+
+
+def test_pool_new_rejects_bad_sizes():
+    L = pkv.lib()
+    assert not L.pkv_pool_new(0, 4, 1, 1, 4, 4, None, 0)
+    assert not L.pkv_pool_new(4, 4, 1, 1, 4, 0, None, 0)
+
+
+def test_known_answers_from_pages():
+    g = read_golden("pool_known_answers.txt")
+    p = pkv.Pool(int(g["pool_blocks"]), 4, 1, 1, 4, device=None)
+    allocs = [int(x) for x in g["allocs"].split()]
+    assert [p.alloc_block() for _ in allocs] == allocs
+    assert p.unref_block(int(g["unref"])) == 0
+    assert p.alloc_block() == int(g["realloc"])
+
+
+def _lib_state(p, seqs):
+    return (p.refcounts().tolist(), p.free_stack().tolist(),
+            [(p.seq_len(s), None if p.seq_pages(s) is None else p.seq_pages(s).tolist())
+             for s in seqs])
+
+
+def _oracle_state(o, seqs):
+    return (o.refcounts().tolist(), o.free_stack().tolist(),
+            [(o.seq_len(s), None if o.seq_pages(s) is None else o.seq_pages(s).tolist())
+             for s in seqs])
+
+
+def test_gate_pool_trace_matches_oracle():
+    """The gate's pool operations (prefill 5, fork, diverge, truncate,
+    re-append) give the same state in the library and the oracle."""
+    gate = synth.TinyGate()
+    o = oracle.Pool(gate.n_blocks, gate.block_size, gate.n_layers,
+                    gate.n_kv_heads, gate.head_dim, with_storage=False)
+    p = pkv.Pool(gate.n_blocks, gate.block_size, gate.n_layers,
+                 gate.n_kv_heads, gate.head_dim, device=None)
+    for impl in (o, p):
+        a = impl.seq_new(gate.max_tokens)
+        assert impl.ensure_append([a], 5) == 0
+        for L in range(gate.n_layers):
+            assert impl.append_layer([a], 5, L, None, None) == 0 if impl is p else True
+        assert impl.advance([a], 5) == 0
+        b = impl.seq_fork(a)
+        assert b == 1
+        for s in (a, b):
+            assert impl.ensure_append([s], 2) == 0
+            assert impl.advance([s], 2) == 0
+        assert impl.seq_truncate(a, 5) == 0
+        assert impl.ensure_append([a], 2) == 0
+        assert impl.advance([a], 2) == 0
+    assert _lib_state(p, [0, 1]) == _oracle_state(o, [0, 1])
+    pa, pb = p.seq_pages(0), p.seq_pages(1)
+    ref = p.refcounts()
+    assert pa[0] == pb[0] and ref[pa[0]] == 2
+    assert pa[1] != pb[1] and ref[pa[1]] == 1 and ref[pb[1]] == 1
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_ops_state_matches_oracle(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.choice([1, 2, 4, 16]))
+    n_blocks = int(rng.integers(8, 64))
+    max_seqs = 6
+    o = oracle.Pool(n_blocks, B, 2, 1, 2, max_seqs=max_seqs, with_storage=False)
+    p = pkv.Pool(n_blocks, B, 2, 1, 2, max_seqs=max_seqs, device=None)
+    perm = rng.permutation(n_blocks)
+    assert o.set_free_order(perm) == p.set_free_order(perm, check=False) == 0
+    raw = []
+    for step in range(200):
+        op = int(rng.integers(0, 9))
+        s = int(rng.integers(-1, max_seqs + 1))
+        if op == 0:
+            mt = int(rng.integers(-1, 80))
+            assert o.seq_new(mt) == p.seq_new(mt)
+        elif op == 1:
+            assert o.seq_fork(s) == p.seq_fork(s)
+        elif op == 2:
+            nl = int(rng.integers(-1, 40))
+            assert o.seq_truncate(s, nl) == p.seq_truncate(s, nl)
+        elif op == 3:
+            assert o.seq_free(s) == p.seq_free(s)
+        elif op == 4:
+            b1, b2 = o.alloc_block(), p.alloc_block()
+            assert b1 == b2
+            if b1 >= 0:
+                raw.append(b1)
+        elif op == 5:
+            if raw and rng.random() < 0.8:
+                b = raw.pop()
+            else:  # an id that is free or out of range: both must refuse it
+                free = o.free_stack().tolist()
+                b = int(rng.choice(free + [-1, n_blocks]))
+            assert o.unref_block(b) == p.unref_block(b)
+        else:
+            M = int(rng.integers(0, 4))
+            batch = [int(x) for x in rng.integers(-1, max_seqs, size=M)]
+            n = int(rng.integers(0, 9))
+            assert o.ensure_append(batch, n) == p.ensure_append(batch, n), (step, batch, n)
+            if op >= 7:
+                layer = int(rng.integers(-1, 3))
+                assert (o.append_layer(batch, n, layer, np.zeros((max(M * n, 1), 2), np.float32),
+                                       np.zeros((max(M * n, 1), 2), np.float32))
+                        == p.append_layer(batch, n, layer, None, None)), (step, batch, n)
+            nadv = n if rng.random() < 0.8 else int(rng.integers(0, 9))
+            assert o.advance(batch, nadv) == p.advance(batch, nadv)
+        assert _lib_state(p, range(max_seqs)) == _oracle_state(o, range(max_seqs)), step
+
+
+def test_ensure_oom_is_atomic():
+    p = pkv.Pool(5, 4, 1, 1, 4, device=None)
+    a, b = p.seq_new(64), p.seq_new(64)
+    assert p.ensure_append([a], 8) == 0 and p.advance([a], 8) == 0
+    before = _lib_state(p, [a, b])
+    assert p.ensure_append([a, b], 9) == pkv.OOM
+    assert _lib_state(p, [a, b]) == before
+
+
+def test_attention_front_checks_order():
+    """Status codes of the attention entry points follow the pages' order
+    (dims, grouping, sequence) before anything else; a metadata-only pool
+    then refuses with BAD_ARG."""
+    L = pkv.lib()
+    p = pkv.Pool(4, 4, 1, 2, 4, device=None)
+    s = np.array([p.seq_new(8)], np.int32)
+    sp = s.ctypes.data_as(pkv._lib.C.c_void_p)
+    dec = L.pkv_attn_paged_decode
+    assert dec(p._h, sp, 0, 0, 4, 2, 4, None, 1.0, None, None, 0, None) == pkv.BAD_DIM
+    assert dec(p._h, sp, 1, 0, 3, 2, 4, None, 1.0, None, None, 0, None) == pkv.BAD_GQA
+    assert dec(p._h, sp, 1, 0, 4, 1, 4, None, 1.0, None, None, 0, None) == pkv.BAD_DIM
+    bad = np.array([3], np.int32)
+    assert dec(p._h, bad.ctypes.data_as(pkv._lib.C.c_void_p), 1, 0, 4, 2, 4, None,
+               1.0, None, None, 0, None) == pkv.ERR_SEQ
+    assert dec(p._h, sp, 1, 1, 4, 2, 4, None, 1.0, None, None, 0, None) == pkv.BAD_ARG
+    assert dec(p._h, sp, 1, 0, 4, 2, 4, None, 1.0, None, None, 0, None) == pkv.BAD_ARG
+    pre = L.pkv_attn_paged_prefill
+    assert pre(p._h, sp, 1, 0, 0, 4, 2, 4, None, 1, 1.0, None, None) == pkv.BAD_DIM
+    assert pre(p._h, sp, 1, 2, 0, 6, 4, 4, None, 1, 1.0, None, None) == pkv.BAD_GQA
