@@ -1,0 +1,343 @@
+"""Benchmark: batched paged-GQA decode on one MI355X.
+
+One step = the whole decode hot path for M=256 sequences, one new token
+each: ensure_append (capacity + copy-on-append), append_layer (scatter of
+the new K/V rows), attn_paged_decode (split decode kernel + split merge,
+page tables uploaded once per step), advance.  Workload: Qwen3-4B-shaped
+attention (32 query heads, 8 kv heads, head_dim 128), float32, 16-row pages
+placed by a seeded random permutation, context lengths log-uniform on
+[1024, 16384].  All inputs are synthetic (seeded numpy) and resident in HBM
+before the timed region.
+
+Prints one JSON line.  ``value`` is the whole-step KV throughput in GB/s
+(algorithmic K+V bytes the step must read, 8192 B per visible key, divided
+by wall time of the timed steps); ``roofline`` is the decode kernel's
+achieved bandwidth from HIP events around each launch against 8 TB/s;
+``cpu_baseline`` is the CPU oracle on a bounded sample of the same workload.
+A secondary object measures chunked prefill (8 x (3584 cached + 512 new))
+against the FP32 MFMA peak.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
+METRIC = ("paged GQA decode: achieved KV HBM GB/s (% peak) + "
+          "seq-tokens/s at M=256")
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_m256",
+                    choices=["decode_m256", "decode_m32"])
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget for the oracle sample")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    return ap.parse_args()
+
+
+class HistoryFiller:
+    """Generates each sequence's seeded history into reusable pinned buffers
+    on worker threads and appends it through the library."""
+
+    def __init__(self, wl, max_rows, workers=8):
+        import torch
+        from concurrent.futures import ThreadPoolExecutor
+        self.torch = torch
+        self.wl = wl
+        self.workers = workers
+        pin = torch.cuda.is_available()
+        self.bufs = []
+        for _ in range(workers):
+            k = torch.empty((max_rows, wl.kv_dim), dtype=torch.float32, pin_memory=pin)
+            v = torch.empty((max_rows, wl.kv_dim), dtype=torch.float32, pin_memory=pin)
+            self.bufs.append((k, v))
+        self.ex = ThreadPoolExecutor(max_workers=workers)
+
+    def fill(self, pool, seqs, n_rows, layer=0):
+        torch = self.torch
+        W = self.workers
+        kd = torch.empty((max(n_rows), self.wl.kv_dim), device="cuda")
+        vd = torch.empty_like(kd)
+        for base in range(0, len(seqs), W):
+            idx = list(range(base, min(base + W, len(seqs))))
+            futs = [self.ex.submit(self.wl.history, r,
+                                   (self.bufs[i][0].numpy(), self.bufs[i][1].numpy()))
+                    for i, r in enumerate(idx)]
+            for i, (r, f) in enumerate(zip(idx, futs)):
+                f.result()
+                n = int(n_rows[r])
+                kd[:n].copy_(self.bufs[i][0][:n], non_blocking=True)
+                vd[:n].copy_(self.bufs[i][1][:n], non_blocking=True)
+                pool.ensure_append([seqs[r]], n, check=True)
+                pool.append_layer([seqs[r]], n, layer, kd[:n], vd[:n], check=True)
+                pool.advance([seqs[r]], n, check=True)
+                torch.cuda.synchronize()  # pinned buffer i is reused next round
+            if base % (8 * W) == 0:
+                log("history %d/%d" % (idx[-1] + 1, len(seqs)))
+        del kd, vd
+
+    def close(self):
+        self.ex.shutdown()
+
+
+def traffic_for(kernel_name, launches_bytes=None):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_traffic.json" % kernel_name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    src = os.path.join(ROOT, "paged_kv_gqa_layer_amd", "csrc", "kernels.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if t.get("kernels_hip_sha256") != sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def bench_decode(args, synth, pkv):
+    import torch
+    mk = synth.decode_m256 if args.workload == "decode_m256" else synth.decode_m32
+    n_steps = args.warmup + args.steps
+    wl = mk(max_steps=n_steps + 1)
+    H, G, D = wl.n_heads, wl.n_kv_heads, wl.head_dim
+    M = wl.M
+    log("workload %s: M=%d, cached rows %d..%d (sum %d), pool %d blocks (%.2f GB)"
+        % (wl.name, M, wl.ctx.min(), wl.ctx.max(), wl.ctx.sum(), wl.n_blocks,
+           pkv.pool_storage_bytes(wl.n_blocks, 16, 1, G, D) / 1e9))
+    pool = pkv.Pool(wl.n_blocks, wl.block_size, 1, G, D, max_seqs=M + 8)
+    pool.set_free_order(wl.free_order())
+    seqs = [pool.seq_new(wl.max_tokens) for _ in range(M)]
+    t0 = time.time()
+    filler = HistoryFiller(wl, int(wl.ctx.max()))
+    filler.fill(pool, seqs, wl.ctx)
+    filler.close()
+    log("history appended in %.1fs" % (time.time() - t0))
+
+    # step inputs, resident in HBM before timing
+    steps = []
+    for t in range(n_steps):
+        q, k, v = wl.step(t)
+        steps.append(tuple(torch.from_numpy(x).cuda() for x in (q, k, v)))
+    out = torch.empty((M, H * D), device="cuda")
+    seqs_np = np.asarray(seqs, np.int32)
+    # workspace for the longest step (contexts grow by one row per step)
+    wsb = int(sum(math.ceil((int(c) + n_steps + 1) / 512) for c in wl.ctx)) * H * (D + 2) * 4
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    scale = wl.scale
+
+    def step(t):
+        q, k, v = steps[t]
+        pool.ensure_append(seqs_np, 1, check=True)
+        pool.append_layer(seqs_np, 1, 0, k, v, check=True)
+        pool.attn_paged_decode(seqs_np, 0, H, G, D, q, scale, out, ws=ws, check=True)
+        pool.advance(seqs_np, 1, check=True)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    pool.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, n_steps):
+        step(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    kv_bytes = 0
+    for t in range(args.warmup, n_steps):
+        kv_bytes += int((wl.ctx.astype(np.int64) + t + 1).sum()) * 2 * wl.kv_dim * 4
+    kern = {}
+    for name, kid in (("append", pkv.K_APPEND), ("decode", pkv.K_DECODE),
+                      ("combine", pkv.K_COMBINE), ("cow", pkv.K_COW)):
+        ms, n = pool.profile_read(kid)
+        kern[name] = {"launches": n, "avg_us": (1e3 * ms / n) if n else 0.0}
+    pool.profile_enable(False)
+    dec_s = kern["decode"]["avg_us"] * 1e-6 * kern["decode"]["launches"]
+    achieved = kv_bytes / dec_s / 1e9
+    gbs = kv_bytes / elapsed / 1e9
+    res = {
+        "wl": wl, "pool": pool, "seqs": seqs, "elapsed": elapsed,
+        "kv_bytes": kv_bytes, "gbs": gbs, "achieved": achieved, "kern": kern,
+        "seq_tok_s": M * args.steps / elapsed,
+    }
+    log("decode: %.3f ms/step, %.0f GB/s step, kernel %.1f us avg -> %.0f GB/s (%.1f%% of peak)"
+        % (1e3 * elapsed / args.steps, gbs, kern["decode"]["avg_us"], achieved,
+           100 * achieved / HBM_PEAK_GBS))
+    return res
+
+
+def cpu_baseline(args, wl, oracle):
+    """Time the oracle on the first sequences of the same workload (decode
+    step 0: every cached row plus the new one), within a wall budget."""
+    q_all, k_all, v_all = wl.step(0)
+    spent, n, kvb = 0.0, 0, 0
+    H, G, D = wl.n_heads, wl.n_kv_heads, wl.head_dim
+    for r in range(wl.M):
+        kh, vh = wl.history(r)
+        K = np.concatenate([kh, k_all[r:r + 1]])
+        V = np.concatenate([vh, v_all[r:r + 1]])
+        t0 = time.perf_counter()
+        rc, _ = oracle.attn_contig(q_all[r:r + 1], K, V, H, G, D, True, wl.scale)
+        spent += time.perf_counter() - t0
+        assert rc == 0
+        n += 1
+        kvb += K.shape[0] * wl.kv_dim * 2 * 4
+        if spent > args.cpu_seconds:
+            break
+    log("cpu oracle: %d sequences in %.2fs" % (n, spent))
+    return {
+        "value": kvb / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": "decode step of sequences 0..%d of %d (%d keys, one thread)"
+                  % (n - 1, wl.M, kvb // (wl.kv_dim * 8)),
+        "seq_tokens_per_s": n / spent,
+    }
+
+
+def bench_prefill(args, synth, pkv):
+    import torch
+    wl = synth.prefill_8x3584p512()
+    H, G, D, M = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.M
+    pool = pkv.Pool(wl.n_blocks, wl.block_size, 1, G, D, max_seqs=M + 4)
+    pool.set_free_order(wl.free_order())
+    seqs = [pool.seq_new(wl.max_tokens) for _ in range(M)]
+    filler = HistoryFiller(wl, wl.cached)
+    filler.fill(pool, seqs, [wl.cached] * M)
+    filler.close()
+    Q = torch.empty((M * wl.chunk, H * D), device="cuda")
+    K = torch.empty((M * wl.chunk, G * D), device="cuda")
+    V = torch.empty_like(K)
+    for r in range(M):
+        q, k, v = wl.chunk_inputs(r)
+        Q[r * wl.chunk:(r + 1) * wl.chunk].copy_(torch.from_numpy(q))
+        K[r * wl.chunk:(r + 1) * wl.chunk].copy_(torch.from_numpy(k))
+        V[r * wl.chunk:(r + 1) * wl.chunk].copy_(torch.from_numpy(v))
+    out = torch.empty_like(Q)
+    seqs_np = np.asarray(seqs, np.int32)
+
+    def step():
+        pool.ensure_append(seqs_np, wl.chunk, check=True)
+        pool.append_layer(seqs_np, wl.chunk, 0, K, V, check=True)
+        pool.attn_paged_prefill(seqs_np, wl.chunk, 0, H, G, D, Q, True, wl.scale,
+                                out, check=True)
+        for s in seqs:  # rewind so the next step appends the same chunk
+            pool.seq_truncate(s, wl.cached, check=True)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    pool.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.prefill_steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms, n = pool.profile_read(pkv.K_PREFILL)
+    pool.profile_enable(False)
+    visible = M * sum(wl.cached + i + 1 for i in range(wl.chunk))
+    flops = 4 * D * H * visible
+    kern_s = ms * 1e-3 / n
+    tf = flops / kern_s / 1e12
+    log("prefill: step %.3f ms, kernel %.3f ms -> %.1f TFLOP/s (%.1f%% of FP32 MFMA peak)"
+        % (1e3 * elapsed / args.prefill_steps, 1e3 * kern_s, tf,
+           100 * tf / FP32_MFMA_PEAK_TFLOPS))
+    pool.close()
+    return {
+        "workload": wl.name, "ms_per_step": 1e3 * elapsed / args.prefill_steps,
+        "steps": args.prefill_steps,
+        "step": "ensure_append(512) + append_layer + attn_paged_prefill + truncate",
+        "kernel_ms": 1e3 * kern_s, "flops_per_step": flops,
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf / FP32_MFMA_PEAK_TFLOPS,
+                     "traffic": None},
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world),
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    sys.path.insert(0, ROOT)
+    import torch
+    import paged_kv_gqa_layer_amd as pkv
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    pkv.lib()  # fail loudly if the HIP library is not built
+
+    d = bench_decode(args, synth, pkv)
+    wl = d["wl"]
+    traffic = traffic_for("decode_fast_kernel")
+    line = {
+        "metric": METRIC,
+        "value": d["gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * d["elapsed"] / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "M": wl.M, "n_heads": wl.n_heads,
+            "n_kv_heads": wl.n_kv_heads, "head_dim": wl.head_dim,
+            "block_size": wl.block_size, "layers": 1,
+            "context_rows": [int(wl.ctx.min()), int(wl.ctx.max())],
+            "mean_total_k": float(wl.ctx.mean() + 1 + args.warmup + (args.steps - 1) / 2),
+            "split_keys": 512, "placement": "random permutation",
+            "step": "ensure_append + append_layer + attn_paged_decode + advance",
+        },
+        "seq_tokens_per_s": d["seq_tok_s"],
+        "pct_hbm_peak": 100.0 * d["gbs"] / HBM_PEAK_GBS,
+        "kv_bytes_per_step": d["kv_bytes"] / args.steps,
+        "kernels_us": {k: v["avg_us"] for k, v in d["kern"].items()},
+        "roofline": {
+            "bound": "hbm", "achieved": d["achieved"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": d["achieved"] / HBM_PEAK_GBS,
+            "traffic": (traffic if traffic is not None else None),
+            "kernel": "decode_fast_kernel<4, PagedMap>",
+            "bytes_per_launch": d["kv_bytes"] / args.steps,
+        },
+    }
+    d["pool"].close()
+    del d
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        line["prefill"] = bench_prefill(args, synth, pkv)
+    if not args.no_cpu_baseline:
+        import oracle
+        line["cpu_baseline"] = cpu_baseline(args, wl, oracle)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

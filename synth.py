@@ -96,8 +96,16 @@ def _rng(seed, *tags):
     return np.random.default_rng([int(seed)] + [int(t) for t in tags])
 
 
-def _normal(rng, shape, sigma):
-    a = rng.standard_normal(shape, dtype=np.float32)
+def _normal(rng, shape, sigma, out=None):
+    """N(0, sigma) float32 of `shape`; written into `out` (a C-contiguous
+    float32 array with at least prod(shape) elements) when given, which
+    draws exactly the same numbers without allocating."""
+    if out is None:
+        a = rng.standard_normal(shape, dtype=np.float32)
+    else:
+        n = int(np.prod(shape))
+        a = out.reshape(-1)[:n].reshape(shape)
+        rng.standard_normal(out=a, dtype=np.float32)
     if sigma != 1.0:
         a *= np.float32(sigma)
     return a
@@ -143,12 +151,14 @@ class DecodeWorkload:
         """Random placement: the order in which the pool hands out ids."""
         return _rng(self.seed, _S_PLACE).permutation(self.n_blocks).astype(np.int64)
 
-    def history(self, r):
-        """(K, V) [ctx[r], kv_dim] float32 for sequence r."""
+    def history(self, r, out=None):
+        """(K, V) [ctx[r], kv_dim] float32 for sequence r (into out=(k, v)
+        buffers when given)."""
         g = _rng(self.seed, _S_HIST, r)
         n = int(self.ctx[r])
-        k = _normal(g, (n, self.kv_dim), self.sigma)
-        v = _normal(g, (n, self.kv_dim), self.sigma)
+        ok, ov = out if out is not None else (None, None)
+        k = _normal(g, (n, self.kv_dim), self.sigma, ok)
+        v = _normal(g, (n, self.kv_dim), self.sigma, ov)
         return k, v
 
     def step(self, t):
@@ -218,10 +228,11 @@ class PrefillWorkload:
     def free_order(self):
         return _rng(self.seed, _S_PLACE).permutation(self.n_blocks).astype(np.int64)
 
-    def history(self, r):
+    def history(self, r, out=None):
         g = _rng(self.seed, _S_HIST, r)
-        k = _normal(g, (self.cached, self.kv_dim), self.sigma)
-        v = _normal(g, (self.cached, self.kv_dim), self.sigma)
+        ok, ov = out if out is not None else (None, None)
+        k = _normal(g, (self.cached, self.kv_dim), self.sigma, ok)
+        v = _normal(g, (self.cached, self.kv_dim), self.sigma, ov)
         return k, v
 
     def chunk_inputs(self, r):
