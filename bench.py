@@ -52,7 +52,25 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the oracle sample")
     ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (calibrates the "
+                         "HBM byte counters) and exit")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain device-to-device copy of known size, for scaling the
+    FETCH_SIZE / WRITE_SIZE counters: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "launches": 3}), flush=True)
 
 
 class HistoryFiller:
@@ -289,6 +307,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
     pkv.lib()  # fail loudly if the HIP library is not built
 
     d = bench_decode(args, synth, pkv)
