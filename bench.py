@@ -187,7 +187,7 @@ def bench_decode(args, synth, pkv):
         kv_bytes += int((wl.ctx.astype(np.int64) + t + 1).sum()) * 2 * wl.kv_dim * 4
     kern = {}
     for name, kid in (("append", pkv.K_APPEND), ("decode", pkv.K_DECODE),
-                      ("combine", pkv.K_COMBINE), ("cow", pkv.K_COW)):
+                      ("merge", pkv.K_MERGE), ("cow", pkv.K_COW)):
         ms, n = pool.profile_read(kid)
         kern[name] = {"launches": n, "avg_us": (1e3 * ms / n) if n else 0.0}
     pool.profile_enable(False)

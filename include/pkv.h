@@ -307,7 +307,7 @@ int32_t pkv_pool_free_stack(pkv_pool *pool, int64_t *out, int32_t cap);
 /* Kernel ids for pkv_profile_read. */
 #define PKV_K_APPEND 0
 #define PKV_K_DECODE 1   /* the split decode kernel */
-#define PKV_K_COMBINE 2  /* the split-merge kernel */
+#define PKV_K_MERGE 2    /* the merge of the decode key splits */
 #define PKV_K_PREFILL 3
 #define PKV_K_COW 4
 #define PKV_K_COUNT 5

@@ -17,13 +17,13 @@ import numpy as np
 
 from . import _lib
 from ._lib import (BAD_ARG, BAD_DIM, BAD_GQA, CAPACITY, DEVICE, ERR_SEQ,
-                   K_APPEND, K_COMBINE, K_COW, K_DECODE, K_PREFILL, OK, OOM,
+                   K_APPEND, K_COW, K_DECODE, K_MERGE, K_PREFILL, OK, OOM,
                    SIZE_MAX, UNSUPPORTED, Contig, PKVError)
 
 __all__ = [
     "Pool", "ContigCache", "PKVError", "lib", "pool_storage_bytes",
     "OK", "BAD_DIM", "BAD_GQA", "ERR_SEQ", "OOM", "CAPACITY", "BAD_ARG",
-    "DEVICE", "UNSUPPORTED", "K_APPEND", "K_DECODE", "K_COMBINE", "K_PREFILL",
+    "DEVICE", "UNSUPPORTED", "K_APPEND", "K_DECODE", "K_MERGE", "K_PREFILL",
     "K_COW",
 ]
 
@@ -103,6 +103,7 @@ class Pool:
                 raise ValueError("bad pool dims")
             self.storage = torch.empty(nbytes, dtype=torch.uint8, device=device)
             ptr = self.storage.data_ptr()
+        self._free = lib().pkv_pool_free  # kept for interpreter shutdown
         self._h = lib().pkv_pool_new(n_blocks, block_size, n_layers, n_kv_heads,
                                      head_dim, max_seqs, ptr, nbytes)
         if not self._h:
@@ -110,7 +111,7 @@ class Pool:
 
     def close(self):
         if getattr(self, "_h", None):
-            lib().pkv_pool_free(self._h)
+            self._free(self._h)
             self._h = None
 
     def __del__(self):

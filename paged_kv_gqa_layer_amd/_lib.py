@@ -21,7 +21,7 @@ BAD_ARG = 6
 DEVICE = 7
 UNSUPPORTED = 8
 
-K_APPEND, K_DECODE, K_COMBINE, K_PREFILL, K_COW = range(5)
+K_APPEND, K_DECODE, K_MERGE, K_PREFILL, K_COW = range(5)
 
 SIZE_MAX = (1 << 64) - 1
 

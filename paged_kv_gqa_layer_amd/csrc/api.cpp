@@ -1,20 +1,22 @@
-// C ABI of libpkv (declared in include/pkv.h): argument checks, the
-// per-call batch descriptor upload, kernel launches and kernel timing.
+// C ABI of libpkv (declared in include/pkv.h): argument checks, device-side
+// pool state, per-call descriptor upload, kernel launches and kernel timing.
 //
-// Descriptor upload.  Each device call needs its batch's lengths, page ids
-// and work list on the GPU.  The host packs them into one int32 blob, copies
-// it into a pinned staging slot and enqueues one H2D copy into a
-// library-owned device buffer (one per call kind) on the caller's stream,
-// so the kernels that follow are stream-ordered after it.  Staging slots
-// rotate through a ring; a slot is rewritten only after the event recorded
-// behind its previous copy has completed.  A blob that is identical to what
-// its kind's device buffer already holds (same pool version, same batch, same
-// call shape) is not sent again, so the layers of one step share one upload.
+// Device-side state of a pool (besides the caller's K/V storage):
+//  - a mirror of every sequence's page table, int32 [max_seqs][stride], kept
+//    current by patch lists (one entry per page-table write on the host,
+//    applied by a small kernel before the next kernel that reads the mirror);
+//  - per batch row, one RowDesc (length, mirror offset, decode split range),
+//    uploaded once per pool version and batch, so every layer of a step
+//    reuses the same upload.
+// Uploads go through a ring of pinned staging slots; a slot is rewritten only
+// after the event recorded behind its previous copy has completed.  All
+// copies and kernels of a pool go to the caller's stream, in call order.
 #include <hip/hip_runtime.h>
 
-#include <cmath>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
+#include <unordered_set>
 #include <vector>
 
 #include "device.hpp"
@@ -25,22 +27,23 @@ namespace {
 
 using pkv::AttnArgs;
 using pkv::ContigMap;
-using pkv::Item;
-using pkv::OutDesc;
 using pkv::PagedMap;
 using pkv::RowDesc;
 
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr int kStageSlots = 8;
-constexpr int32_t kNoSplit = 1 << 30;
 
-enum Kind { kAppend = 0, kDecode = 1, kPrefill = 2, kCow = 3, kNumKinds = 4 };
+enum Buf { kRows = 0, kPatch = 1, kCow = 2, kNumBufs = 3 };
 
 inline int32_t ceil_div(int64_t a, int64_t b) {
   return static_cast<int32_t>((a + b - 1) / b);
 }
 
-// Pinned host staging ring + per-kind device buffers + upload cache.
+int32_t dev_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_DEVICE; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// Pinned staging ring, small device buffers, timing.
 struct DeviceCtx {
   struct Slot {
     void* host = nullptr;
@@ -48,19 +51,18 @@ struct DeviceCtx {
     hipEvent_t ev = nullptr;
     bool pending = false;
   };
-  struct Buf {
+  struct DevBuf {
     void* ptr = nullptr;
     size_t cap = 0;
-    bool valid = false;  // holds `key`
+    bool valid = false;  // holds the blob described by `key`
     std::vector<int64_t> key;
   };
   Slot slot[kStageSlots];
   int next = 0;
-  Buf buf[kNumKinds];
+  DevBuf buf[kNumBufs];
   hipStream_t last_stream = nullptr;
   bool used = false;
 
-  // profiling
   bool prof_on = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[PKV_K_COUNT];
 
@@ -75,7 +77,7 @@ struct DeviceCtx {
     }
     for (auto& b : buf) {
       if (b.ptr) (void)hipFree(b.ptr);
-      b = Buf();
+      b = DevBuf();
     }
     clear_prof();
     used = false;
@@ -102,28 +104,34 @@ struct DeviceCtx {
     return hipSuccess;
   }
 
-  // Copy blob into buffer `kind` (unless it already holds `key`).
-  hipError_t upload(int kind, const std::vector<int32_t>& blob,
+  // Device buffer `b` with room for `bytes` (its old content is dropped).
+  hipError_t reserve(int b, size_t bytes, hipStream_t st) {
+    DevBuf& d = buf[b];
+    if (bytes <= d.cap) return hipSuccess;
+    hipError_t e = hipStreamSynchronize(st);  // old buffer may still be read
+    if (e != hipSuccess) return e;
+    if (d.ptr) (void)hipFree(d.ptr);
+    d = DevBuf();
+    const size_t cap = bytes < 65536 ? 65536 : bytes + bytes / 2;
+    if ((e = hipMalloc(&d.ptr, cap)) != hipSuccess) return e;
+    d.cap = cap;
+    return hipSuccess;
+  }
+
+  // Copy `blob` into device buffer `b` (skipped if it already holds `key`;
+  // an empty key never matches).
+  hipError_t upload(int b, const std::vector<int32_t>& blob,
                     const std::vector<int64_t>& key, hipStream_t st,
                     int32_t** dev) {
-    Buf& b = buf[kind];
-    const size_t bytes = blob.size() * sizeof(int32_t);
-    if (b.valid && b.key == key) {
-      *dev = static_cast<int32_t*>(b.ptr);
+    DevBuf& d = buf[b];
+    if (!key.empty() && d.valid && d.key == key) {
+      *dev = static_cast<int32_t*>(d.ptr);
       return hipSuccess;
     }
-    b.valid = false;
-    hipError_t e;
-    if (bytes > b.cap) {
-      // the old buffer may still be read by enqueued kernels
-      if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
-      if (b.ptr) (void)hipFree(b.ptr);
-      b.ptr = nullptr;
-      b.cap = 0;
-      size_t cap = bytes < 65536 ? 65536 : bytes + bytes / 2;
-      if ((e = hipMalloc(&b.ptr, cap)) != hipSuccess) return e;
-      b.cap = cap;
-    }
+    d.valid = false;
+    const size_t bytes = std::max<size_t>(blob.size(), 1) * sizeof(int32_t);
+    hipError_t e = reserve(b, bytes, st);
+    if (e != hipSuccess) return e;
     Slot& s = slot[next];
     next = (next + 1) % kStageSlots;
     if (s.pending) {
@@ -136,20 +144,21 @@ struct DeviceCtx {
       if (s.host) (void)hipHostFree(s.host);
       s.host = nullptr;
       s.cap = 0;
-      size_t cap = bytes < 65536 ? 65536 : bytes + bytes / 2;
+      const size_t cap = bytes < 65536 ? 65536 : bytes + bytes / 2;
       if ((e = hipHostMalloc(&s.host, cap, hipHostMallocDefault)) != hipSuccess) return e;
       s.cap = cap;
     }
-    if (bytes) {
-      std::memcpy(s.host, blob.data(), bytes);
-      if ((e = hipMemcpyAsync(b.ptr, s.host, bytes, hipMemcpyHostToDevice, st)) != hipSuccess)
+    if (!blob.empty()) {
+      std::memcpy(s.host, blob.data(), blob.size() * sizeof(int32_t));
+      if ((e = hipMemcpyAsync(d.ptr, s.host, blob.size() * sizeof(int32_t),
+                              hipMemcpyHostToDevice, st)) != hipSuccess)
         return e;
       if ((e = hipEventRecord(s.ev, st)) != hipSuccess) return e;
       s.pending = true;
     }
-    b.key = key;
-    b.valid = true;
-    *dev = static_cast<int32_t*>(b.ptr);
+    d.key = key;
+    d.valid = !key.empty();
+    *dev = static_cast<int32_t*>(d.ptr);
     return hipSuccess;
   }
 
@@ -161,8 +170,13 @@ struct DeviceCtx {
     hipEvent_t a = nullptr, b = nullptr;
     ProfScope(DeviceCtx* c_, int k_, hipStream_t st_) : c(c_), k(k_), st(st_) {
       if (!c->prof_on) return;
-      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
-        a = b = nullptr;
+      if (hipEventCreate(&a) != hipSuccess) {
+        a = nullptr;
+        return;
+      }
+      if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        a = nullptr;
         return;
       }
       (void)hipEventRecord(a, st);
@@ -175,10 +189,6 @@ struct DeviceCtx {
   };
 };
 
-int32_t dev_status(hipError_t e) { return e == hipSuccess ? PKV_OK : PKV_ERR_DEVICE; }
-
-hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
-
 // Shared by the contiguous-twin calls (no pool object to hang state on).
 DeviceCtx& contig_ctx() {
   static DeviceCtx* c = new DeviceCtx();  // lives until process exit
@@ -189,64 +199,16 @@ std::mutex& contig_mutex() {
   return m;
 }
 
-// Work-list builders -------------------------------------------------------
-
-// Blob layout: RowDesc[M] | Item[W] | OutDesc[Mo] | pages[]
-struct Blob {
-  std::vector<int32_t> v;
-  size_t rows_off = 0, items_off = 0, outs_off = 0, pages_off = 0;
-  int32_t n_items = 0, n_outs = 0;
-  bool any_split = false;
-};
-
-// Decode/prefill work items for rows with the given total_k values.
-// fast_decode: one item per 512-key split of each row (n_q == 1).
-// otherwise: one item per (row, query), all keys (no split).
-void build_items(Blob& bl, const std::vector<int32_t>& total_k, int32_t n_q,
-                 bool fast_decode, std::vector<int32_t>& items,
-                 std::vector<int32_t>& outs) {
-  items.clear();
-  outs.clear();
-  bl.any_split = false;
-  const int32_t M = static_cast<int32_t>(total_k.size());
-  int32_t n_items = 0;
-  for (int32_t r = 0; r < M; ++r) {
-    for (int32_t i = 0; i < n_q; ++i) {
-      const int32_t nsp = fast_decode ? ceil_div(total_k[r], pkv::kDecodeSplit) : 1;
-      outs.push_back(n_items);
-      outs.push_back(nsp);
-      if (nsp > 1) bl.any_split = true;
-      for (int32_t s = 0; s < nsp; ++s) {
-        items.push_back(r);
-        items.push_back(i);
-        items.push_back(s);
-        items.push_back(nsp);
-        ++n_items;
-      }
-    }
-  }
-  bl.n_items = n_items;
-  bl.n_outs = M * n_q;
-}
-
-void assemble(Blob& bl, const std::vector<int32_t>& rows,
-              const std::vector<int32_t>& items, const std::vector<int32_t>& outs,
-              const std::vector<int32_t>& pages) {
-  bl.v.clear();
-  bl.rows_off = 0;
-  bl.v.insert(bl.v.end(), rows.begin(), rows.end());
-  bl.items_off = bl.v.size();
-  bl.v.insert(bl.v.end(), items.begin(), items.end());
-  bl.outs_off = bl.v.size();
-  bl.v.insert(bl.v.end(), outs.begin(), outs.end());
-  bl.pages_off = bl.v.size();
-  bl.v.insert(bl.v.end(), pages.begin(), pages.end());
-  if (bl.v.empty()) bl.v.push_back(0);
-}
-
-size_t workspace_bytes_for(const Blob& bl, int32_t n_heads, int32_t head_dim) {
-  if (!bl.any_split) return 0;
-  return static_cast<size_t>(bl.n_items) * n_heads * (head_dim + 2) * sizeof(float);
+// One RowDesc per batch row: start position, mirror offset (or slot) and
+// the row's decode split items (total_k = start + 1, kDecodeSplit keys each).
+void push_row(std::vector<int32_t>& v, int32_t start, int32_t pt_off,
+              int32_t* n_items) {
+  const int32_t nsp = ceil_div(static_cast<int64_t>(start) + 1, pkv::kDecodeSplit);
+  v.push_back(start);
+  v.push_back(pt_off);
+  v.push_back(*n_items);
+  v.push_back(nsp);
+  *n_items += nsp;
 }
 
 }  // namespace
@@ -259,23 +221,108 @@ struct pkv_pool {
   size_t storage_bytes = 0;
   int64_t block_floats = 0;
   DeviceCtx dev;
-  // scratch reused across calls
-  std::vector<int32_t> rows, items, outs, pages, tk;
-  Blob blob;
+  int32_t* mirror = nullptr;  // [max_seqs][stride]
+  int64_t stride = 0;
+  // the row blob currently in dev.buf[kRows]
+  std::vector<int32_t> rows;
+  int32_t n_items = 0;
+  int32_t max_splits = 0;
+  std::vector<int64_t> rows_key;
+  std::vector<int32_t> scratch;
+  std::unordered_set<int64_t> seen;
 
   pkv_pool(int32_t nb, int32_t bs, int32_t nl, int32_t g, int32_t d, int32_t ms)
       : meta(nb, bs, nl, g, d, ms) {}
+  ~pkv_pool() {
+    dev.release();
+    if (mirror) (void)hipFree(mirror);
+  }
 };
-
 
 namespace {
 
-PagedMap make_paged_map(const pkv_pool* p, int32_t layer, const int32_t* pages_dev) {
+// Bring the page-table mirror up to date on `st`: (re)allocate it when a
+// sequence may outgrow its stride, then apply the pending patches.
+hipError_t sync_mirror(pkv_pool* p, hipStream_t st) {
+  auto& m = p->meta;
+  hipError_t e;
+  const int64_t need = std::max<int64_t>(m.max_pages_seen(), 1);
+  if (!p->mirror || need > p->stride) {
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+    if (p->mirror) (void)hipFree(p->mirror);
+    p->mirror = nullptr;
+    const int64_t stride = (need + 63) / 64 * 64;
+    if ((e = hipMalloc(&p->mirror, static_cast<size_t>(m.max_seqs()) * stride *
+                                       sizeof(int32_t))) != hipSuccess)
+      return e;
+    p->stride = stride;
+    p->rows_key.clear();  // row descriptors hold mirror offsets
+    // the new mirror needs every live page-table entry
+    auto& pt = m.patches();
+    pt.clear();
+    for (int32_t s = 0; s < m.max_seqs(); ++s) {
+      const pkv::SeqMeta* q = m.seq(s);
+      if (!q) continue;
+      for (int32_t i = 0; i < static_cast<int32_t>(q->pages.size()); ++i)
+        pt.push_back({s, i, q->pages[i]});
+    }
+  }
+  auto& pt = m.patches();
+  if (pt.empty()) return hipSuccess;
+  // The patch kernel writes entries in parallel, so keep only the last write
+  // of each (sequence, page) entry (a fork's share followed by a
+  // copy-on-append replacement, for example).
+  p->scratch.clear();
+  p->seen.clear();
+  for (auto it = pt.rbegin(); it != pt.rend(); ++it) {
+    if (!p->seen.insert(static_cast<int64_t>(it->seq) * p->stride + it->page).second)
+      continue;
+    p->scratch.push_back(it->seq);
+    p->scratch.push_back(it->page);
+    p->scratch.push_back(it->block);
+  }
+  pt.clear();
+  int32_t* d = nullptr;
+  if ((e = p->dev.upload(kPatch, p->scratch, {}, st, &d)) != hipSuccess) return e;
+  return pkv::launch_patch(p->mirror, d, static_cast<int32_t>(p->scratch.size() / 3),
+                           p->stride, st);
+}
+
+// Row descriptors of this batch on the device (uploaded unless the device
+// copy already describes this batch at this pool version).
+hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M,
+                     hipStream_t st, const RowDesc** rows_dev) {
+  hipError_t e = sync_mirror(p, st);
+  if (e != hipSuccess) return e;
+  std::vector<int64_t> key;
+  key.reserve(M + 2);
+  key.push_back(static_cast<int64_t>(p->meta.version()));
+  key.push_back(p->stride);
+  key.insert(key.end(), seqs, seqs + M);
+  if (key != p->rows_key) {
+    p->rows.clear();
+    p->n_items = 0;
+    p->max_splits = 0;
+    for (int32_t r = 0; r < M; ++r) {
+      const pkv::SeqMeta* q = p->meta.seq(seqs[r]);
+      push_row(p->rows, q->seq_len, static_cast<int32_t>(seqs[r] * p->stride),
+               &p->n_items);
+      p->max_splits = std::max(p->max_splits, p->rows.back());
+    }
+  }
+  int32_t* d = nullptr;
+  if ((e = p->dev.upload(kRows, p->rows, key, st, &d)) != hipSuccess) return e;
+  p->rows_key = key;
+  *rows_dev = reinterpret_cast<const RowDesc*>(d);
+  return hipSuccess;
+}
+
+PagedMap make_paged_map(const pkv_pool* p, int32_t layer) {
   const auto& m = p->meta;
   const int64_t G = m.n_kv_heads(), B = m.block_size(), D = m.head_dim();
   PagedMap pm;
   pm.base = p->storage;
-  pm.pages = pages_dev;
+  pm.pages = p->mirror;
   pm.block_stride = p->block_floats;
   pm.layer_off = static_cast<int64_t>(layer) * 2 * G * B * D;
   pm.head_stride = B * D;
@@ -303,59 +350,58 @@ ContigMap make_contig_map(const pkv_contig* c, int32_t layer) {
   return cm;
 }
 
-// Common attention launch (decode: n_q == 1 and decode == true).
+// Decode partial results a batch needs: only the specialised kernel splits.
+size_t partial_bytes(int32_t n_items, int32_t max_splits, int32_t n_heads,
+                     int32_t head_dim) {
+  if (max_splits <= 1) return 0;
+  return static_cast<size_t>(n_items) * n_heads * (head_dim + 2) * sizeof(float);
+}
+
+// Launch attention (decode: n_q == 1 and decode == true).
 template <class Map>
-int32_t run_attention(DeviceCtx& dev, const Map& map, const Blob& bl,
-                      const int32_t* blob_dev, const float* Q, float* out,
-                      void* ws, int32_t n_heads, int32_t n_kv_heads,
+int32_t run_attention(DeviceCtx& dev, const Map& map, const RowDesc* rows,
+                      int32_t n_items, int32_t max_splits, const float* Q,
+                      float* out, void* ws, int32_t n_heads, int32_t n_kv_heads,
                       int32_t head_dim, int32_t n_q, int32_t causal,
                       float scale, int32_t M, int32_t block_size, bool decode,
                       hipStream_t st) {
   const int32_t group = n_heads / n_kv_heads;
   AttnArgs a;
-  a.rows = reinterpret_cast<const RowDesc*>(blob_dev + bl.rows_off);
-  a.items = reinterpret_cast<const Item*>(blob_dev + bl.items_off);
-  a.outs = reinterpret_cast<const OutDesc*>(blob_dev + bl.outs_off);
+  a.rows = rows;
   a.Q = Q;
   a.out = out;
   a.part_o = static_cast<float*>(ws);
   a.part_ml = ws ? static_cast<float*>(ws) +
-                       static_cast<size_t>(bl.n_items) * n_heads * head_dim
+                       static_cast<size_t>(n_items) * n_heads * head_dim
                  : nullptr;
+  a.n_rows = M;
   a.n_heads = n_heads;
   a.n_kv_heads = n_kv_heads;
   a.head_dim = head_dim;
   a.n_q = n_q;
   a.causal = causal;
   a.qscale = static_cast<float>(static_cast<double>(scale) * kLog2e);
-  a.n_items = bl.n_items;
-  a.n_outs = bl.n_outs;
-  a.split = kNoSplit;
+  a.n_items = n_items;
   hipError_t e;
   if (decode && pkv::fast_decode_ok(head_dim, group, block_size)) {
     {
       DeviceCtx::ProfScope ps(&dev, PKV_K_DECODE, st);
-      e = pkv::launch_decode_fast(map, a, group, st);
+      if ((e = pkv::launch_decode_fast(map, a, group, st)) != hipSuccess)
+        return PKV_ERR_DEVICE;
     }
-    if (e != hipSuccess) return PKV_ERR_DEVICE;
-    if (bl.any_split) {
-      DeviceCtx::ProfScope ps(&dev, PKV_K_COMBINE, st);
-      e = pkv::launch_combine(a, st);
-      if (e != hipSuccess) return PKV_ERR_DEVICE;
-    }
-    return PKV_OK;
+    if (max_splits <= 1) return PKV_OK;
+    DeviceCtx::ProfScope ps(&dev, PKV_K_MERGE, st);
+    return dev_status(pkv::launch_merge(a, st));
   }
   if (!decode && pkv::fast_prefill_ok(head_dim, group, block_size)) {
     DeviceCtx::ProfScope ps(&dev, PKV_K_PREFILL, st);
-    e = pkv::launch_prefill_mfma(map, a, M, st);
-    return dev_status(e);
+    return dev_status(pkv::launch_prefill_mfma(map, a, st));
   }
   if (group > 16) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(group) * head_dim * 2 + group * 64 > 16384)
     return PKV_ERR_UNSUPPORTED;  // generic kernel keeps q and o in LDS
   DeviceCtx::ProfScope ps(&dev, decode ? PKV_K_DECODE : PKV_K_PREFILL, st);
-  e = pkv::launch_generic(map, a, group, st);
-  return dev_status(e);
+  return dev_status(pkv::launch_generic(map, a, group, st));
 }
 
 // Common front checks of the attention calls, in the pages' order.
@@ -365,39 +411,6 @@ int32_t attn_front_checks(int32_t M, int32_t n_q, int32_t n_heads,
     return PKV_ERR_BAD_DIM;
   if (n_heads % n_kv_heads != 0) return PKV_ERR_BAD_GQA;
   return PKV_OK;
-}
-
-// Build the attention blob for pool rows (total_k = seq_len + n_q).
-void pool_attn_blob(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n_q,
-                    bool fast_decode) {
-  const int32_t B = p->meta.block_size();
-  p->rows.clear();
-  p->pages.clear();
-  p->tk.clear();
-  for (int32_t r = 0; r < M; ++r) {
-    const pkv::SeqMeta* q = p->meta.seq(seqs[r]);
-    const int32_t total_k = q->seq_len + n_q;
-    const int32_t np = ceil_div(total_k, B);
-    p->rows.push_back(total_k);
-    p->rows.push_back(static_cast<int32_t>(p->pages.size()));
-    p->rows.push_back(np);
-    p->rows.push_back(0);
-    p->pages.insert(p->pages.end(), q->pages.begin(), q->pages.begin() + np);
-    p->tk.push_back(total_k);
-  }
-  build_items(p->blob, p->tk, n_q, fast_decode, p->items, p->outs);
-  assemble(p->blob, p->rows, p->items, p->outs, p->pages);
-}
-
-std::vector<int64_t> blob_key(uint64_t version, int32_t kind_arg, int32_t n,
-                              const int32_t* seqs, int32_t M) {
-  std::vector<int64_t> k;
-  k.reserve(M + 3);
-  k.push_back(static_cast<int64_t>(version));
-  k.push_back(kind_arg);
-  k.push_back(n);
-  for (int32_t r = 0; r < M; ++r) k.push_back(seqs[r]);
-  return k;
 }
 
 }  // namespace
@@ -450,6 +463,7 @@ pkv_pool* pkv_pool_new(int32_t n_blocks, int32_t block_size, int32_t n_layers,
   p->storage_bytes = storage_bytes;
   p->block_floats = static_cast<int64_t>(n_layers) * 2 * n_kv_heads *
                     block_size * head_dim;
+  p->meta.track_patches(storage_dev != nullptr);
   return p;
 }
 
@@ -506,10 +520,7 @@ int32_t pkv_ensure_append(pkv_pool* pool, const int32_t* seqs, int32_t M,
     pairs.push_back(c.dst);
   }
   int32_t* dev = nullptr;
-  std::vector<int64_t> nokey{-1};  // never matches a later COW upload
-  pool->dev.buf[kCow].valid = false;
-  if (pool->dev.upload(kCow, pairs, nokey, st, &dev) != hipSuccess) return PKV_ERR_DEVICE;
-  pool->dev.buf[kCow].valid = false;
+  if (pool->dev.upload(kCow, pairs, {}, st, &dev) != hipSuccess) return PKV_ERR_DEVICE;
   DeviceCtx::ProfScope ps(&pool->dev, PKV_K_COW, st);
   return dev_status(pkv::launch_cow(pool->storage, dev,
                                     static_cast<int32_t>(cows.size()),
@@ -528,34 +539,13 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (!K_new_dev || !V_new_dev) return PKV_ERR_BAD_ARG;
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
-
-  // rows: start position and the pages the new rows land in
-  const int32_t B = pool->meta.block_size();
-  pool->rows.clear();
-  pool->pages.clear();
-  for (int32_t r = 0; r < M; ++r) {
-    const pkv::SeqMeta* q = pool->meta.seq(seqs[r]);
-    const int32_t np = ceil_div(static_cast<int64_t>(q->seq_len) + n_new, B);
-    pool->rows.push_back(q->seq_len);
-    pool->rows.push_back(static_cast<int32_t>(pool->pages.size()));
-    pool->rows.push_back(np);
-    pool->rows.push_back(0);
-    pool->pages.insert(pool->pages.end(), q->pages.begin(), q->pages.begin() + np);
-  }
-  pool->items.clear();
-  pool->outs.clear();
-  assemble(pool->blob, pool->rows, pool->items, pool->outs, pool->pages);
-  int32_t* dev = nullptr;
-  if (pool->dev.upload(kAppend, pool->blob.v,
-                       blob_key(pool->meta.version(), 0, n_new, seqs, M), st,
-                       &dev) != hipSuccess)
-    return PKV_ERR_DEVICE;
-  const PagedMap pm = make_paged_map(pool, layer, dev + pool->blob.pages_off);
+  const RowDesc* rows = nullptr;
+  if (pool_rows(pool, seqs, M, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
+  const PagedMap pm = make_paged_map(pool, layer);
   DeviceCtx::ProfScope ps(&pool->dev, PKV_K_APPEND, st);
   return dev_status(pkv::launch_append(
-      pm, reinterpret_cast<const RowDesc*>(dev + pool->blob.rows_off), K_new_dev,
-      V_new_dev, M, n_new, pool->meta.n_kv_heads() * pool->meta.head_dim(),
-      pool->meta.head_dim(), st));
+      pm, rows, K_new_dev, V_new_dev, M, n_new,
+      pool->meta.n_kv_heads() * pool->meta.head_dim(), pool->meta.head_dim(), st));
 }
 
 int32_t pkv_advance(pkv_pool* pool, const int32_t* seqs, int32_t M, int32_t n) {
@@ -569,18 +559,15 @@ size_t pkv_decode_workspace_bytes(pkv_pool* pool, const int32_t* seqs,
   const auto& m = pool->meta;
   if (n_heads % m.n_kv_heads() != 0) return static_cast<size_t>(-1);
   if (m.check_batch(seqs, M) != PKV_OK) return static_cast<size_t>(-1);
-  const bool fast = pkv::fast_decode_ok(m.head_dim(), n_heads / m.n_kv_heads(),
-                                        m.block_size());
-  if (!fast) return 0;
-  int64_t items = 0;
-  bool split = false;
+  if (!pkv::fast_decode_ok(m.head_dim(), n_heads / m.n_kv_heads(), m.block_size()))
+    return 0;
+  int32_t items = 0, max_sp = 0;
+  std::vector<int32_t> tmp;
   for (int32_t r = 0; r < M; ++r) {
-    const int32_t nsp = ceil_div(m.seq(seqs[r])->seq_len + 1, pkv::kDecodeSplit);
-    items += nsp;
-    split = split || nsp > 1;
+    push_row(tmp, m.seq(seqs[r])->seq_len, 0, &items);
+    max_sp = std::max(max_sp, tmp.back());
   }
-  if (!split) return 0;
-  return static_cast<size_t>(items) * n_heads * (m.head_dim() + 2) * sizeof(float);
+  return partial_bytes(items, max_sp, n_heads, m.head_dim());
 }
 
 int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
@@ -597,22 +584,16 @@ int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (!pool->storage) return PKV_ERR_BAD_ARG;
   if (int32_t rc = m.check_rows(seqs, M, 1)) return rc;
   if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
-  const int32_t group = n_heads / n_kv_heads;
-  const bool fast = pkv::fast_decode_ok(head_dim, group, m.block_size());
-  pool_attn_blob(pool, seqs, M, 1, fast);
-  const size_t need = workspace_bytes_for(pool->blob, n_heads, head_dim);
+  const size_t need = pkv_decode_workspace_bytes(pool, seqs, M, n_heads);
   if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
-  int32_t* dev = nullptr;
-  if (pool->dev.upload(kDecode, pool->blob.v,
-                       blob_key(m.version(), 1, n_heads, seqs, M), st,
-                       &dev) != hipSuccess)
-    return PKV_ERR_DEVICE;
-  const PagedMap pm = make_paged_map(pool, layer, dev + pool->blob.pages_off);
-  return run_attention(pool->dev, pm, pool->blob, dev, Q_dev, out_dev, ws_dev,
-                       n_heads, n_kv_heads, head_dim, 1, 1, scale, M,
-                       m.block_size(), true, st);
+  const RowDesc* rows = nullptr;
+  if (pool_rows(pool, seqs, M, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
+  const PagedMap pm = make_paged_map(pool, layer);
+  return run_attention(pool->dev, pm, rows, pool->n_items, pool->max_splits, Q_dev,
+                       out_dev, ws_dev, n_heads, n_kv_heads, head_dim, 1, 1, scale,
+                       M, m.block_size(), true, st);
 }
 
 int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
@@ -629,18 +610,14 @@ int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (!pool->storage) return PKV_ERR_BAD_ARG;
   if (int32_t rc = m.check_rows(seqs, M, n_q)) return rc;
   if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
-  pool_attn_blob(pool, seqs, M, n_q, false);
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
-  int32_t* dev = nullptr;
-  if (pool->dev.upload(kPrefill, pool->blob.v,
-                       blob_key(m.version(), 2, n_q, seqs, M), st,
-                       &dev) != hipSuccess)
-    return PKV_ERR_DEVICE;
-  const PagedMap pm = make_paged_map(pool, layer, dev + pool->blob.pages_off);
-  return run_attention(pool->dev, pm, pool->blob, dev, Q_dev, out_dev, nullptr,
-                       n_heads, n_kv_heads, head_dim, n_q, causal ? 1 : 0,
-                       scale, M, m.block_size(), false, st);
+  const RowDesc* rows = nullptr;
+  if (pool_rows(pool, seqs, M, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
+  const PagedMap pm = make_paged_map(pool, layer);
+  return run_attention(pool->dev, pm, rows, pool->n_items, 1, Q_dev, out_dev,
+                       nullptr, n_heads, n_kv_heads, head_dim, n_q,
+                       causal ? 1 : 0, scale, M, m.block_size(), false, st);
 }
 
 // ---------------------------------------------------------------- contiguous
@@ -656,26 +633,23 @@ size_t pkv_contig_bytes(int32_t n_slots, int32_t n_layers, int32_t n_kv_heads,
 
 namespace {
 
-// Rows for contiguous calls: pt_off holds the slot.
+// Rows for contiguous calls (pt_off = slot); checks slots and lengths.
 int32_t contig_rows(const pkv_contig* c, const int32_t* slots,
                     const int32_t* seq_lens, int32_t M, int32_t n,
-                    std::vector<int32_t>& rows, std::vector<int32_t>* tk,
-                    bool total) {
+                    std::vector<int32_t>& rows, int32_t* n_items,
+                    int32_t* max_splits) {
   if (!slots || !seq_lens) return PKV_ERR_BAD_ARG;
   rows.clear();
-  if (tk) tk->clear();
+  *n_items = 0;
+  *max_splits = 0;
   for (int32_t r = 0; r < M; ++r) {
     if (slots[r] < 0 || slots[r] >= c->n_slots) return PKV_ERR_SEQ;
     for (int32_t r2 = 0; r2 < r; ++r2)
       if (slots[r2] == slots[r]) return PKV_ERR_SEQ;
     if (seq_lens[r] < 0) return PKV_ERR_BAD_ARG;
     if (static_cast<int64_t>(seq_lens[r]) + n > c->max_seq) return PKV_ERR_SEQ;
-    const int32_t tkr = seq_lens[r] + n;
-    rows.push_back(total ? tkr : seq_lens[r]);
-    rows.push_back(slots[r]);
-    rows.push_back(ceil_div(tkr, c->block_size));
-    rows.push_back(0);
-    if (tk) tk->push_back(tkr);
+    push_row(rows, seq_lens[r], slots[r], n_items);
+    *max_splits = std::max(*max_splits, rows.back());
   }
   return PKV_OK;
 }
@@ -691,18 +665,15 @@ int32_t pkv_contig_append(const pkv_contig* cache, const int32_t* slots,
   if (layer < 0 || layer >= cache->n_layers) return PKV_ERR_BAD_ARG;
   if (!K_new_dev || !V_new_dev) return PKV_ERR_BAD_ARG;
   std::lock_guard<std::mutex> g(contig_mutex());
-  std::vector<int32_t> rows, none;
-  if (int32_t rc = contig_rows(cache, slots, seq_lens, M, n_new, rows, nullptr, false))
+  std::vector<int32_t> rows;
+  int32_t n_items = 0, max_sp = 0;
+  if (int32_t rc = contig_rows(cache, slots, seq_lens, M, n_new, rows, &n_items, &max_sp))
     return rc;
-  Blob bl;
-  assemble(bl, rows, none, none, none);
   DeviceCtx& dev = contig_ctx();
   const hipStream_t st = as_stream(stream);
   if (dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
   int32_t* d = nullptr;
-  dev.buf[kAppend].valid = false;
-  if (dev.upload(kAppend, bl.v, {-1}, st, &d) != hipSuccess) return PKV_ERR_DEVICE;
-  dev.buf[kAppend].valid = false;
+  if (dev.upload(kRows, rows, {}, st, &d) != hipSuccess) return PKV_ERR_DEVICE;
   const ContigMap cm = make_contig_map(cache, layer);
   return dev_status(pkv::launch_append(cm, reinterpret_cast<const RowDesc*>(d),
                                        K_new_dev, V_new_dev, M, n_new,
@@ -717,15 +688,14 @@ size_t pkv_contig_decode_workspace_bytes(const int32_t* seq_lens, int32_t M,
       n_heads % n_kv_heads != 0)
     return static_cast<size_t>(-1);
   if (!pkv::fast_decode_ok(head_dim, n_heads / n_kv_heads, 16)) return 0;
-  int64_t items = 0;
-  bool split = false;
+  int32_t items = 0, max_sp = 0;
+  std::vector<int32_t> tmp;
   for (int32_t r = 0; r < M; ++r) {
-    const int32_t nsp = ceil_div(static_cast<int64_t>(seq_lens[r]) + 1, pkv::kDecodeSplit);
-    items += nsp;
-    split = split || nsp > 1;
+    if (seq_lens[r] < 0) return static_cast<size_t>(-1);
+    push_row(tmp, seq_lens[r], 0, &items);
+    max_sp = std::max(max_sp, tmp.back());
   }
-  if (!split) return 0;
-  return static_cast<size_t>(items) * n_heads * (head_dim + 2) * sizeof(float);
+  return partial_bytes(items, max_sp, n_heads, head_dim);
 }
 
 namespace {
@@ -742,25 +712,24 @@ int32_t contig_attention(const pkv_contig* cache, const int32_t* slots,
   if (layer < 0 || layer >= cache->n_layers) return PKV_ERR_BAD_ARG;
   if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
   std::lock_guard<std::mutex> g(contig_mutex());
-  std::vector<int32_t> rows, items, outs, none, tk;
-  if (int32_t rc = contig_rows(cache, slots, seq_lens, M, n_q, rows, &tk, true)) return rc;
+  std::vector<int32_t> rows;
+  int32_t n_items = 0, max_sp = 0;
+  if (int32_t rc = contig_rows(cache, slots, seq_lens, M, n_q, rows, &n_items, &max_sp))
+    return rc;
   const int32_t group = n_heads / n_kv_heads;
   const bool fast = decode && pkv::fast_decode_ok(head_dim, group, cache->block_size);
-  Blob bl;
-  build_items(bl, tk, n_q, fast, items, outs);
-  assemble(bl, rows, items, outs, none);
-  const size_t need = workspace_bytes_for(bl, n_heads, head_dim);
-  if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
+  if (fast) {
+    const size_t need = partial_bytes(n_items, max_sp, n_heads, head_dim);
+    if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
+  }
   DeviceCtx& dev = contig_ctx();
   const hipStream_t st = as_stream(stream);
   if (dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
-  const int kind = decode ? kDecode : kPrefill;
   int32_t* d = nullptr;
-  dev.buf[kind].valid = false;
-  if (dev.upload(kind, bl.v, {-1}, st, &d) != hipSuccess) return PKV_ERR_DEVICE;
-  dev.buf[kind].valid = false;
+  if (dev.upload(kRows, rows, {}, st, &d) != hipSuccess) return PKV_ERR_DEVICE;
   const ContigMap cm = make_contig_map(cache, layer);
-  return run_attention(dev, cm, bl, d, Q_dev, out_dev, ws_dev, n_heads,
+  return run_attention(dev, cm, reinterpret_cast<const RowDesc*>(d), n_items,
+                       decode ? max_sp : 1, Q_dev, out_dev, ws_dev, n_heads,
                        n_kv_heads, head_dim, n_q, causal, scale, M,
                        cache->block_size, decode, st);
 }

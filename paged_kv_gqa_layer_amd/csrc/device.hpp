@@ -1,11 +1,13 @@
 // Descriptors shared by the host launch code and the gfx950 kernels, plus the
 // host-side launcher declarations.
 //
-// A call's batch is described by one int32 blob uploaded per call:
-//   RowDesc[M]  per sequence row: total_k, page-list offset, split count...
-//   Item[W]     per work item (sequence row, query, key split)
-//   OutDesc[Mo] per output row: first item and split count (split merge)
-//   pages[]     the batch's page tables, concatenated (block ids)
+// Device-resident state of a pool: the K/V storage (caller memory) and a
+// mirror of every sequence's page table, int32 [max_seqs][stride], kept up
+// to date by small patch lists.  Per call the kernels get one RowDesc per
+// batch row (uploaded once per pool version and batch, so all layers of a
+// step share it).  Decode work items (row, key split) are numbered row by
+// row; the decode kernel finds an item's row by binary search over
+// first_item.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,22 +17,11 @@
 namespace pkv {
 
 struct RowDesc {
-  int32_t total_k;  // keys this row attends over (append: first position)
-  int32_t pt_off;   // paged: offset of the row's page ids; contiguous: slot
-  int32_t n_pages;  // page ids present for this row
-  int32_t pad;
-};
-
-struct Item {
-  int32_t row;    // sequence row
-  int32_t qi;     // query within the row (0 for decode)
-  int32_t split;  // key split index
-  int32_t nsp;    // number of splits of this (row, query)
-};
-
-struct OutDesc {
-  int32_t first_item;
-  int32_t n_splits;
+  int32_t start;       // rows cached before this call (= seq_len)
+  int32_t pt_off;      // paged: offset of the row's page table in the mirror;
+                       // contiguous: the cache slot
+  int32_t first_item;  // decode: first split item of this row
+  int32_t n_splits;    // decode: split items of this row (n_q = 1)
 };
 
 // Address of one page (block_size consecutive positions) of one kv head:
@@ -38,7 +29,7 @@ struct OutDesc {
 // at + t * head_dim.
 struct PagedMap {
   float* base;
-  const int32_t* pages;
+  const int32_t* pages;  // the page-table mirror
   int64_t block_stride;  // floats per block (all layers)
   int64_t layer_off;     // floats from block start to this layer
   int64_t head_stride;   // floats between kv heads
@@ -83,12 +74,11 @@ inline bool fast_prefill_ok(int32_t head_dim, int32_t group, int32_t block) {
 
 struct AttnArgs {
   const RowDesc* rows;
-  const Item* items;
-  const OutDesc* outs;
   const float* Q;
   float* out;
-  float* part_o;   // [items][n_heads][head_dim]
-  float* part_ml;  // [items][n_heads][2]
+  float* part_o;      // [items][n_heads][head_dim]   (decode with splits)
+  float* part_ml;     // [items][n_heads][2]
+  int32_t n_rows;
   int32_t n_heads;
   int32_t n_kv_heads;
   int32_t head_dim;
@@ -96,11 +86,12 @@ struct AttnArgs {
   int32_t causal;
   float qscale;  // scale * log2(e): scores are kept in base-2 units
   int32_t n_items;
-  int32_t n_outs;
-  int32_t split;  // generic kernel: key positions per split item
 };
 
 // Launchers (kernels.hip).  Each returns hipSuccess or the launch error.
+hipError_t launch_patch(int32_t* mirror, const int32_t* patches, int32_t n,
+                        int64_t stride, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 hipError_t launch_append(const PagedMap& m, const RowDesc* rows,
                          const float* K, const float* V, int32_t M, int32_t n,
                          int32_t kv_dim, int32_t head_dim, hipStream_t st);
@@ -113,14 +104,15 @@ hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
 hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
+// Merges the key splits of every row with more than one (after decode_fast).
+hipError_t launch_merge(const AttnArgs& a, hipStream_t st);
 hipError_t launch_generic(const PagedMap& m, const AttnArgs& a,
                           int32_t group, hipStream_t st);
 hipError_t launch_generic(const ContigMap& m, const AttnArgs& a,
                           int32_t group, hipStream_t st);
-hipError_t launch_combine(const AttnArgs& a, hipStream_t st);
 hipError_t launch_prefill_mfma(const PagedMap& m, const AttnArgs& a,
-                               int32_t M, hipStream_t st);
+                               hipStream_t st);
 hipError_t launch_prefill_mfma(const ContigMap& m, const AttnArgs& a,
-                               int32_t M, hipStream_t st);
+                               hipStream_t st);
 
 }  // namespace pkv

@@ -62,6 +62,15 @@ __device__ __forceinline__ float4 ld4(const float* p) {
   return *reinterpret_cast<const float4*>(p);
 }
 
+// Streaming load: K/V bytes a decode wave reads are used by that wave only,
+// so they are fetched with the non-temporal hint (they are not kept in the
+// caches for other workgroups).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld4_stream(const float* p) {
+  const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(r.x, r.y, r.z, r.w);
+}
+
 __device__ __forceinline__ float dot8(const float4& ka, const float4& kb,
                                       const float (&qa)[4],
                                       const float (&qb)[4]) {
@@ -93,7 +102,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int32_t r = static_cast<int32_t>(rt / n);
     const int32_t t = static_cast<int32_t>(rt - (int64_t)r * n);
     const RowDesc rd = rows[r];
-    const int32_t pos = rd.total_k + t;
+    const int32_t pos = rd.start + t;
     const int32_t kvh = c / head_dim;
     const int32_t d = c - kvh * head_dim;
     float* dst = m.page(rd, pos / m.block_size, kvh) +
@@ -145,6 +154,56 @@ __global__ __launch_bounds__(256) void cow_kernel(float* base,
 // (m, l, o) over the positions it sees; the four row states are merged at
 // the end of the split with cross-row shuffles.
 // ---------------------------------------------------------------------------
+// Split merge for one (row, kv head), run by one 64-lane wave:
+// out = sum_s w_s o_s / sum_s w_s l_s with w_s = 2^(m_s - max_s m_s).
+// Lanes own split indices for the statistics and head dims (2 each) for the
+// weighted sum, which runs over the splits in ascending order.
+// One wave merges one head j of the group.
+__device__ __forceinline__ void merge_head(const AttnArgs& a, int32_t row,
+                                           int32_t head, int32_t first_item,
+                                           int32_t nsp, int lane) {
+  constexpr int D = 128;
+  constexpr int U = 8;  // split rows loaded together
+  const int64_t H = a.n_heads;
+  const int64_t h0 = (int64_t)first_item * H + head;
+  float mx = kNegInf;
+  for (int32_t s = lane; s < nsp; s += 64) mx = fmaxf(mx, a.part_ml[(h0 + s * H) * 2]);
+  mx = wave_max(mx);
+  float lw = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int32_t s0 = 0; s0 < nsp; s0 += 64) {
+    const int32_t s = s0 + lane;
+    float w = 0.f;
+    if (s < nsp) {
+      w = fast_exp2(a.part_ml[(h0 + s * H) * 2] - mx);
+      lw = fmaf(w, a.part_ml[(h0 + s * H) * 2 + 1], lw);
+    }
+    const int32_t cnt = min(64, nsp - s0);
+    const float* base = a.part_o + (h0 + (int64_t)s0 * H) * D + 2 * lane;
+    int32_t t = 0;
+    for (; t + U <= cnt; t += U) {
+      float2 ov[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        ov[u] = *reinterpret_cast<const float2*>(base + (int64_t)(t + u) * H * D);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wt = __shfl(w, t + u);
+        o0 = fmaf(wt, ov[u].x, o0);
+        o1 = fmaf(wt, ov[u].y, o1);
+      }
+    }
+    for (; t < cnt; ++t) {
+      const float wt = __shfl(w, t);
+      const float2 ov = *reinterpret_cast<const float2*>(base + (int64_t)t * H * D);
+      o0 = fmaf(wt, ov.x, o0);
+      o1 = fmaf(wt, ov.y, o1);
+    }
+  }
+  const float L = wave_sum(lw);
+  *reinterpret_cast<float2*>(a.out + ((int64_t)row * H + head) * D + 2 * lane) =
+      make_float2(o0 / L, o1 / L);
+}
+
 template <int GROUP, class Map>
 __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   constexpr int D = 128;
@@ -153,14 +212,22 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   const int32_t G = a.n_kv_heads;
   const int32_t item_idx = blockIdx.x / G;
   const int32_t kvh = blockIdx.x - item_idx * G;
-  const Item it = a.items[item_idx];
-  const RowDesc rd = a.rows[it.row];
+  // the row owning this item: last row with first_item <= item_idx
+  int32_t lo = 0, hi = a.n_rows - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (a.rows[mid].first_item <= item_idx) lo = mid; else hi = mid - 1;
+  }
+  const int32_t row = lo;
+  const RowDesc rd = a.rows[row];
+  const int32_t split = item_idx - rd.first_item;
+  const int32_t nsp = rd.n_splits;
   const int lane = threadIdx.x;
   const int rr = lane >> 4;
   const int c = lane & 15;
 
-  const int32_t total_k = rd.total_k;
-  const int32_t k_begin = it.split * kDecodeSplit;
+  const int32_t total_k = rd.start + 1;
+  const int32_t k_begin = split * kDecodeSplit;
   const int32_t k_end = min(total_k, k_begin + kDecodeSplit);
   const int32_t p_begin = k_begin / B;
   const int32_t p_end = (k_end + B - 1) / B;
@@ -168,7 +235,7 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   float qa[GROUP][4], qb[GROUP][4];
   {
     const float* qrow =
-        a.Q + ((int64_t)it.row * a.n_heads + (int64_t)kvh * GROUP) * D;
+        a.Q + ((int64_t)row * a.n_heads + (int64_t)kvh * GROUP) * D;
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
       const float4 x = ld4(qrow + j * D + 4 * c);
@@ -206,10 +273,10 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
       const int t = 4 * i + rr;
       const int off = t * D + 4 * c;
       if (t < n_valid) {
-        ka[i] = ld4(kp + off);
-        kb[i] = ld4(kp + off + 64);
-        va[i] = ld4(vp + off);
-        vb[i] = ld4(vp + off + 64);
+        ka[i] = ld4_stream(kp + off);
+        kb[i] = ld4_stream(kp + off + 64);
+        va[i] = ld4_stream(vp + off);
+        vb[i] = ld4_stream(vp + off + 64);
       } else {
         ka[i] = kb[i] = va[i] = vb[i] = zero4;
       }
@@ -315,8 +382,8 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   }
 
   // Row rr writes heads j with j % 4 == rr.
-  if (it.nsp == 1) {
-    float* orow = a.out + ((int64_t)it.row * a.n_heads + (int64_t)kvh * GROUP) * D;
+  if (nsp == 1) {
+    float* orow = a.out + ((int64_t)row * a.n_heads + (int64_t)kvh * GROUP) * D;
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
       if ((j & 3) == rr) {
@@ -352,9 +419,26 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   }
 }
 
+// Split merge kernel: one wave per (row, kv head) of a row with splits.  A
+// separate launch (rather than the last split merging in place) keeps the
+// partials coherent across XCDs through the kernel boundary; an in-kernel
+// merge needs a device-scope release per split, which costs more than this
+// launch.
+// One workgroup per row, one wave per query head (block of 256 threads walks
+// the row's heads four at a time).
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+  const int32_t row = blockIdx.x;
+  const RowDesc rd = a.rows[row];
+  if (rd.n_splits <= 1) return;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  for (int32_t head = w; head < a.n_heads; head += 4)
+    merge_head(a, row, head, rd.first_item, rd.n_splits, lane);
+}
+
 // ---------------------------------------------------------------------------
 // Generic attention (any head_dim, group, page size; decode or prefill): one
-// wave per (work item = row x query x key split, kv head).  Lanes take 64
+// wave per (query row, kv head) over all its visible keys.  Lanes take 64
 // keys at a time for the scores; for the weighted sum they take dims.
 // ---------------------------------------------------------------------------
 constexpr int kGenericMaxGroup = 16;
@@ -365,21 +449,22 @@ __global__ __launch_bounds__(64) void generic_kernel(Map m, AttnArgs a,
   extern __shared__ float sh[];
   const int32_t D = a.head_dim;
   const int32_t G = a.n_kv_heads;
-  const int32_t item_idx = blockIdx.x / G;
+  const int32_t item_idx = blockIdx.x / G;  // = row * n_q + query
   const int32_t kvh = blockIdx.x - item_idx * G;
-  const Item it = a.items[item_idx];
-  const RowDesc rd = a.rows[it.row];
+  const int32_t row = item_idx / a.n_q;
+  const int32_t qi = item_idx - row * a.n_q;
+  const RowDesc rd = a.rows[row];
   const int lane = threadIdx.x;
   float* q_sh = sh;                // [group][D]
   float* o_sh = q_sh + group * D;  // [group][D]
   float* p_sh = o_sh + group * D;  // [group][64]
 
-  const int32_t total_k = rd.total_k;
-  const int32_t q_pos = total_k - a.n_q + it.qi;
+  const int32_t total_k = rd.start + a.n_q;
+  const int32_t q_pos = total_k - a.n_q + qi;
   const int32_t vis = a.causal ? q_pos + 1 : total_k;
-  const int32_t k_begin = it.split * a.split;
-  const int32_t k_end = min(vis, k_begin + a.split);
-  const int64_t out_row = (int64_t)it.row * a.n_q + it.qi;
+  const int32_t k_begin = 0;
+  const int32_t k_end = vis;
+  const int64_t out_row = item_idx;
 
   const float* qrow = a.Q + (out_row * a.n_heads + (int64_t)kvh * group) * D;
   for (int32_t e = lane; e < group * D; e += 64) {
@@ -440,59 +525,29 @@ __global__ __launch_bounds__(64) void generic_kernel(Map m, AttnArgs a,
     __syncthreads();
   }
 
-  if (it.nsp == 1) {
-    float* orow = a.out + (out_row * a.n_heads + (int64_t)kvh * group) * D;
-    for (int32_t d = lane; d < D; d += 64) {
+  float* orow = a.out + (out_row * a.n_heads + (int64_t)kvh * group) * D;
+  for (int32_t d = lane; d < D; d += 64) {
 #pragma unroll
-      for (int j = 0; j < kGenericMaxGroup; ++j)
-        if (j < group) orow[j * D + d] = o_sh[j * D + d] / lrun[j];
-    }
-  } else {
-    const int64_t hbase = (int64_t)item_idx * a.n_heads + (int64_t)kvh * group;
-    for (int32_t d = lane; d < D; d += 64) {
-#pragma unroll
-      for (int j = 0; j < kGenericMaxGroup; ++j)
-        if (j < group) a.part_o[(hbase + j) * D + d] = o_sh[j * D + d];
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < kGenericMaxGroup; ++j) {
-        if (j < group) {
-          a.part_ml[(hbase + j) * 2 + 0] = mrun[j];
-          a.part_ml[(hbase + j) * 2 + 1] = lrun[j];
-        }
-      }
-    }
+    for (int j = 0; j < kGenericMaxGroup; ++j)
+      if (j < group) orow[j * D + d] = o_sh[j * D + d] / lrun[j];
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split merge: out = sum_s w_s o_s / sum_s w_s l_s, w_s = 2^(m_s - max m),
-// in ascending split order (fixed, so results do not depend on scheduling).
+// Page-table mirror patches: mirror[seq * stride + page] = block.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
-  const int32_t h = blockIdx.x;
-  const int32_t o = blockIdx.y;
-  const OutDesc od = a.outs[o];
-  if (od.n_splits <= 1) return;
-  const int32_t D = a.head_dim;
-  const float* ml = a.part_ml;
-  float M = kNegInf;
-  for (int32_t s = 0; s < od.n_splits; ++s)
-    M = fmaxf(M, ml[((int64_t)(od.first_item + s) * a.n_heads + h) * 2]);
-  float L = 0.f;
-  for (int32_t s = 0; s < od.n_splits; ++s) {
-    const int64_t i = ((int64_t)(od.first_item + s) * a.n_heads + h) * 2;
-    L = fmaf(ml[i + 1], fast_exp2(ml[i] - M), L);
-  }
-  for (int32_t d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.f;
-    for (int32_t s = 0; s < od.n_splits; ++s) {
-      const int64_t hi = (int64_t)(od.first_item + s) * a.n_heads + h;
-      acc = fmaf(a.part_o[hi * D + d], fast_exp2(ml[hi * 2] - M), acc);
-    }
-    a.out[((int64_t)o * a.n_heads + h) * D + d] = acc / L;
-  }
+__global__ __launch_bounds__(256) void patch_kernel(int32_t* mirror,
+                                                    const int32_t* __restrict__ p,
+                                                    int32_t n, int64_t stride) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) mirror[p[3 * i] * stride + p[3 * i + 1]] = p[3 * i + 2];
+}
+
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n,
+                                                       int32_t v) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -536,7 +591,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(Map m, AttnArgs a,
   const int32_t kvh = rem / n_qt;
   const int32_t qt = rem - kvh * n_qt;
   const RowDesc rd = a.rows[row];
-  const int32_t total_k = rd.total_k;
+  const int32_t total_k = rd.start + a.n_q;
   const int32_t n_q = a.n_q;
 
   const int tid = threadIdx.x;
@@ -721,26 +776,44 @@ hipError_t decode_fast_impl(const Map& m, const AttnArgs& a, int32_t group,
   return hipGetLastError();
 }
 
+hipError_t merge_impl(const AttnArgs& a, hipStream_t st) {
+  merge_kernel<<<a.n_rows, 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
 template <class Map>
 hipError_t generic_impl(const Map& m, const AttnArgs& a, int32_t group,
                         hipStream_t st) {
   if (group > kGenericMaxGroup) return hipErrorInvalidValue;
   const size_t lds = sizeof(float) * (2 * (size_t)group * a.head_dim + (size_t)group * 64);
-  const dim3 grid(a.n_items * a.n_kv_heads);
+  const dim3 grid(a.n_rows * a.n_q * a.n_kv_heads);
   generic_kernel<Map><<<grid, 64, lds, st>>>(m, a, group);
   return hipGetLastError();
 }
 
 template <class Map>
-hipError_t prefill_impl(const Map& m, const AttnArgs& a, int32_t M,
-                        hipStream_t st) {
+hipError_t prefill_impl(const Map& m, const AttnArgs& a, hipStream_t st) {
   const int32_t n_qt = (a.n_q + kPrefillQTile - 1) / kPrefillQTile;
-  const int32_t n_wg = M * a.n_kv_heads * n_qt;
+  const int32_t n_wg = a.n_rows * a.n_kv_heads * n_qt;
   prefill_mfma_kernel<Map><<<n_wg, 256, 0, st>>>(m, a, n_qt, n_wg);
   return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_patch(int32_t* mirror, const int32_t* patches, int32_t n,
+                        int64_t stride, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  patch_kernel<<<(n + 255) / 256, 256, 0, st>>>(mirror, patches, n, stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  fill_i32_kernel<<<static_cast<unsigned>(want < 4096 ? want : 4096), 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
 
 hipError_t launch_append(const PagedMap& m, const RowDesc* rows, const float* K,
                          const float* V, int32_t M, int32_t n, int32_t kv_dim,
@@ -774,6 +847,9 @@ hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st) {
   return decode_fast_impl(m, a, group, st);
 }
+hipError_t launch_merge(const AttnArgs& a, hipStream_t st) {
+  return merge_impl(a, st);
+}
 hipError_t launch_generic(const PagedMap& m, const AttnArgs& a, int32_t group,
                           hipStream_t st) {
   return generic_impl(m, a, group, st);
@@ -782,18 +858,13 @@ hipError_t launch_generic(const ContigMap& m, const AttnArgs& a, int32_t group,
                           hipStream_t st) {
   return generic_impl(m, a, group, st);
 }
-hipError_t launch_combine(const AttnArgs& a, hipStream_t st) {
-  const dim3 grid(a.n_heads, a.n_outs);
-  combine_kernel<<<grid, 128, 0, st>>>(a);
-  return hipGetLastError();
-}
-hipError_t launch_prefill_mfma(const PagedMap& m, const AttnArgs& a, int32_t M,
+hipError_t launch_prefill_mfma(const PagedMap& m, const AttnArgs& a,
                                hipStream_t st) {
-  return prefill_impl(m, a, M, st);
+  return prefill_impl(m, a, st);
 }
 hipError_t launch_prefill_mfma(const ContigMap& m, const AttnArgs& a,
-                               int32_t M, hipStream_t st) {
-  return prefill_impl(m, a, M, st);
+                               hipStream_t st) {
+  return prefill_impl(m, a, st);
 }
 
 }  // namespace pkv

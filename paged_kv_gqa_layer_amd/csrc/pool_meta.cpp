@@ -39,6 +39,15 @@ void PoolMeta::drop_ref(int32_t b) {
   if (refcnt_[b] > 0 && --refcnt_[b] == 0) free_.push_back(b);
 }
 
+// Every page-table write goes through here so the device mirror can follow.
+void PoolMeta::set_page(int32_t s, SeqMeta& q, int32_t p, int32_t block) {
+  if (p == static_cast<int32_t>(q.pages.size()))
+    q.pages.push_back(block);
+  else
+    q.pages[p] = block;
+  if (track_) patches_.push_back({s, p, block});
+}
+
 int64_t PoolMeta::alloc_block() {
   if (free_.empty()) return -1;
   ++version_;
@@ -93,6 +102,7 @@ int32_t PoolMeta::seq_new(int32_t max_tokens) {
   q.max_tokens = max_tokens;
   q.pages.clear();
   q.pages.reserve(pages_for(max_tokens, block_size_));
+  max_pages_seen_ = std::max(max_pages_seen_, pages_for(max_tokens, block_size_));
   ++version_;
   return s;
 }
@@ -124,8 +134,12 @@ int32_t PoolMeta::seq_fork(int32_t s) {
   dst.seq_len = src->seq_len;
   dst.max_tokens = src->max_tokens;
   const int32_t shared = pages_for(src->seq_len, block_size_);
-  dst.pages.assign(src->pages.begin(), src->pages.begin() + shared);
-  for (int32_t b : dst.pages) ++refcnt_[b];
+  dst.pages.clear();
+  for (int32_t p = 0; p < shared; ++p) {
+    const int32_t b = src->pages[p];  // src stays valid: c != s
+    set_page(c, dst, p, b);
+    ++refcnt_[b];
+  }
   ++version_;
   return c;
 }
@@ -195,11 +209,12 @@ int32_t PoolMeta::ensure_append(const int32_t* seqs, int32_t M, int32_t n,
       if (refcnt_[old] > 1) {
         const int32_t fresh = pop();
         --refcnt_[old];  // stays >= 1: it was shared
-        q.pages[p] = fresh;
+        set_page(seqs[r], q, p, fresh);
         if (cows) cows->push_back({old, fresh});
       }
     }
-    while (static_cast<int32_t>(q.pages.size()) < want) q.pages.push_back(pop());
+    while (static_cast<int32_t>(q.pages.size()) < want)
+      set_page(seqs[r], q, static_cast<int32_t>(q.pages.size()), pop());
   }
   ++version_;
   return kOk;

@@ -50,6 +50,14 @@ struct CowCopy {
   int32_t dst;
 };
 
+// One page-table entry that changed since the device mirror was last
+// brought up to date: page `page` of sequence `seq` now names `block`.
+struct PagePatch {
+  int32_t seq;
+  int32_t page;
+  int32_t block;
+};
+
 class PoolMeta {
  public:
   PoolMeta(int32_t n_blocks, int32_t block_size, int32_t n_layers,
@@ -88,12 +96,20 @@ class PoolMeta {
   const std::vector<int32_t>& refcounts() const { return refcnt_; }
   const std::vector<int32_t>& free_stack() const { return free_; }
 
+  // Page-table entries changed since the last take_patches(), in order.
+  // Recording is off until enabled (metadata-only pools never enable it).
+  void track_patches(bool on) { track_ = on; patches_.clear(); }
+  std::vector<PagePatch>& patches() { return patches_; }
+  // Largest page-table length any sequence created so far may reach.
+  int32_t max_pages_seen() const { return max_pages_seen_; }
+
  private:
   SeqMeta* live(int32_t s);
   int32_t lowest_free_id() const;
   void release_from(SeqMeta& q, int32_t keep_pages);
   int32_t pop();
   void drop_ref(int32_t b);
+  void set_page(int32_t s, SeqMeta& q, int32_t p, int32_t block);
 
   int32_t n_blocks_, block_size_, n_layers_, n_kv_heads_, head_dim_, max_seqs_;
   std::vector<int32_t> refcnt_;
@@ -102,6 +118,9 @@ class PoolMeta {
   mutable std::vector<uint64_t> stamp_;  // duplicate detection in batches
   mutable uint64_t stamp_gen_ = 0;
   uint64_t version_ = 0;
+  bool track_ = false;
+  std::vector<PagePatch> patches_;
+  int32_t max_pages_seen_ = 0;
 };
 
 }  // namespace pkv

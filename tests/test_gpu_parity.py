@@ -334,3 +334,36 @@ def test_errors_leave_device_path_untouched():
     assert pool.attn_paged_decode([s], 0, 30, 8, 128, q[:, :3840], 0.1,
                                   out[:, :3840]) == pkv.BAD_GQA
     assert pool.ensure_append([s], 65) == pkv.CAPACITY
+
+
+@pytest.mark.parametrize("prefix,n_forks", [(37, 5), (16, 3), (5, 4)])
+def test_forks_copy_on_append_in_first_step(prefix, n_forks):
+    """Forks of a prefix whose last page is partial all append in the same
+    step: the first n-1 copy the shared tail, the last keeps it.  Every fork
+    must see exactly its own history (regression: the page-table patches of
+    the fork and of the copy hit the same entry)."""
+    H, G, D = 32, 8, 128
+    rng = np.random.default_rng(prefix * 10 + n_forks)
+    pk = rng.standard_normal((prefix, G * D)).astype(np.float32)
+    pv = rng.standard_normal((prefix, G * D)).astype(np.float32)
+    pool = pkv.Pool(64, 16, 1, G, D, max_seqs=n_forks + 2)
+    pool.set_free_order(rng.permutation(64))
+    parent = pool.seq_new(prefix + 8)
+    fill_history(pool, [parent], lambda r: (pk, pv))
+    forks = [pool.seq_fork(parent) for _ in range(n_forks)]
+    assert pool.seq_free(parent) == 0
+    q = rng.standard_normal((n_forks, H * D)).astype(np.float32)
+    k = rng.standard_normal((n_forks, G * D)).astype(np.float32)
+    v = rng.standard_normal((n_forks, G * D)).astype(np.float32)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    out = decode_step(pool, forks, q, k, v, H, G, D, scale)
+    got = out.cpu().numpy()
+    for f in range(n_forks):
+        rc, ref = oracle.attn_contig(q[f:f + 1], np.concatenate([pk, k[f:f + 1]]),
+                                     np.concatenate([pv, v[f:f + 1]]), H, G, D, True,
+                                     scale)
+        assert rc == 0
+        assert_close(got[f:f + 1], ref, "fork %d" % f)
+    tails = [pool.seq_pages(s)[prefix // 16] for s in forks]
+    if prefix % 16:
+        assert len(set(tails)) == n_forks
