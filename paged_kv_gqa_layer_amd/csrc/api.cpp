@@ -199,16 +199,45 @@ std::mutex& contig_mutex() {
   return m;
 }
 
-// One RowDesc per batch row: start position, mirror offset (or slot) and
-// the row's decode split items (total_k = start + 1, kDecodeSplit keys each).
-void push_row(std::vector<int32_t>& v, int32_t start, int32_t pt_off,
-              int32_t* n_items) {
-  const int32_t nsp = ceil_div(static_cast<int64_t>(start) + 1, pkv::kDecodeSplit);
-  v.push_back(start);
-  v.push_back(pt_off);
-  v.push_back(*n_items);
-  v.push_back(nsp);
-  *n_items += nsp;
+// What a row blob holds beyond the RowDescs (see device.hpp).
+struct RowPlan {
+  int32_t n_items = 0;      // decode items = partial-result slots
+  int32_t n_full = 0;       // full-split items
+  int32_t max_splits = 0;
+  size_t tail_off = 0;      // int32 offset of tail_rows in the blob
+};
+
+// Row blob: RowDesc[M] then tail_rows.  rowinfo(r) gives (start, pt_off);
+// the decode plan assumes total_k = start + 1 and kDecodeSplit keys/split.
+template <class F>
+RowPlan build_rows(std::vector<int32_t>& v, int32_t M, F rowinfo) {
+  RowPlan pl;
+  v.assign(static_cast<size_t>(M) * pkv::kRowInts, 0);
+  std::vector<std::pair<int32_t, int32_t>> tails;  // (partial keys, row)
+  int32_t slots = 0;
+  for (int32_t r = 0; r < M; ++r) {
+    const std::pair<int32_t, int32_t> info = rowinfo(r);
+    const int64_t total_k = static_cast<int64_t>(info.first) + 1;
+    const int32_t nsp = ceil_div(total_k, pkv::kDecodeSplit);
+    const int32_t rem = static_cast<int32_t>(total_k % pkv::kDecodeSplit);
+    int32_t* d = v.data() + static_cast<size_t>(r) * pkv::kRowInts;
+    d[0] = info.first;
+    d[1] = info.second;
+    d[2] = pl.n_full;
+    d[3] = nsp;
+    d[4] = slots;
+    pl.n_full += rem ? nsp - 1 : nsp;
+    slots += nsp;
+    pl.max_splits = std::max(pl.max_splits, nsp);
+    if (rem) tails.emplace_back(rem, r);
+  }
+  std::stable_sort(tails.begin(), tails.end(),
+                   [](const std::pair<int32_t, int32_t>& x,
+                      const std::pair<int32_t, int32_t>& y) { return x.first > y.first; });
+  pl.tail_off = v.size();
+  for (const auto& t : tails) v.push_back(t.second);
+  pl.n_items = slots;
+  return pl;
 }
 
 }  // namespace
@@ -225,8 +254,7 @@ struct pkv_pool {
   int64_t stride = 0;
   // the row blob currently in dev.buf[kRows]
   std::vector<int32_t> rows;
-  int32_t n_items = 0;
-  int32_t max_splits = 0;
+  RowPlan plan;
   std::vector<int64_t> rows_key;
   std::vector<int32_t> scratch;
   std::unordered_set<int64_t> seen;
@@ -291,7 +319,7 @@ hipError_t sync_mirror(pkv_pool* p, hipStream_t st) {
 // Row descriptors of this batch on the device (uploaded unless the device
 // copy already describes this batch at this pool version).
 hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M,
-                     hipStream_t st, const RowDesc** rows_dev) {
+                     hipStream_t st, const int32_t** rows_dev) {
   hipError_t e = sync_mirror(p, st);
   if (e != hipSuccess) return e;
   std::vector<int64_t> key;
@@ -300,20 +328,15 @@ hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M,
   key.push_back(p->stride);
   key.insert(key.end(), seqs, seqs + M);
   if (key != p->rows_key) {
-    p->rows.clear();
-    p->n_items = 0;
-    p->max_splits = 0;
-    for (int32_t r = 0; r < M; ++r) {
-      const pkv::SeqMeta* q = p->meta.seq(seqs[r]);
-      push_row(p->rows, q->seq_len, static_cast<int32_t>(seqs[r] * p->stride),
-               &p->n_items);
-      p->max_splits = std::max(p->max_splits, p->rows.back());
-    }
+    p->plan = build_rows(p->rows, M, [&](int32_t r) {
+      return std::make_pair(p->meta.seq(seqs[r])->seq_len,
+                            static_cast<int32_t>(seqs[r] * p->stride));
+    });
   }
   int32_t* d = nullptr;
   if ((e = p->dev.upload(kRows, p->rows, key, st, &d)) != hipSuccess) return e;
   p->rows_key = key;
-  *rows_dev = reinterpret_cast<const RowDesc*>(d);
+  *rows_dev = d;
   return hipSuccess;
 }
 
@@ -351,29 +374,30 @@ ContigMap make_contig_map(const pkv_contig* c, int32_t layer) {
 }
 
 // Decode partial results a batch needs: only the specialised kernel splits.
-size_t partial_bytes(int32_t n_items, int32_t max_splits, int32_t n_heads,
-                     int32_t head_dim) {
-  if (max_splits <= 1) return 0;
-  return static_cast<size_t>(n_items) * n_heads * (head_dim + 2) * sizeof(float);
+size_t partial_bytes(const RowPlan& pl, int32_t n_heads, int32_t head_dim) {
+  if (pl.max_splits <= 1) return 0;
+  return static_cast<size_t>(pl.n_items) * n_heads * (head_dim + 2) * sizeof(float);
 }
 
-// Launch attention (decode: n_q == 1 and decode == true).
+// Launch attention (decode: n_q == 1 and decode == true).  rows_dev points
+// at a row blob laid out by build_rows with plan `pl`.
 template <class Map>
-int32_t run_attention(DeviceCtx& dev, const Map& map, const RowDesc* rows,
-                      int32_t n_items, int32_t max_splits, const float* Q,
-                      float* out, void* ws, int32_t n_heads, int32_t n_kv_heads,
-                      int32_t head_dim, int32_t n_q, int32_t causal,
-                      float scale, int32_t M, int32_t block_size, bool decode,
-                      hipStream_t st) {
+int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
+                      const RowPlan& pl, const float* Q, float* out, void* ws,
+                      int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                      int32_t n_q, int32_t causal, float scale, int32_t M,
+                      int32_t block_size, bool decode, hipStream_t st) {
   const int32_t group = n_heads / n_kv_heads;
   AttnArgs a;
-  a.rows = rows;
+  a.rows = reinterpret_cast<const RowDesc*>(rows_dev);
+  a.tail_rows = rows_dev + pl.tail_off;
   a.Q = Q;
   a.out = out;
   a.part_o = static_cast<float*>(ws);
   a.part_ml = ws ? static_cast<float*>(ws) +
-                       static_cast<size_t>(n_items) * n_heads * head_dim
+                       static_cast<size_t>(pl.n_items) * n_heads * head_dim
                  : nullptr;
+  a.n_full_items = pl.n_full;
   a.n_rows = M;
   a.n_heads = n_heads;
   a.n_kv_heads = n_kv_heads;
@@ -381,7 +405,7 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const RowDesc* rows,
   a.n_q = n_q;
   a.causal = causal;
   a.qscale = static_cast<float>(static_cast<double>(scale) * kLog2e);
-  a.n_items = n_items;
+  a.n_items = pl.n_items;
   hipError_t e;
   if (decode && pkv::fast_decode_ok(head_dim, group, block_size)) {
     {
@@ -389,7 +413,7 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const RowDesc* rows,
       if ((e = pkv::launch_decode_fast(map, a, group, st)) != hipSuccess)
         return PKV_ERR_DEVICE;
     }
-    if (max_splits <= 1) return PKV_OK;
+    if (pl.max_splits <= 1) return PKV_OK;
     DeviceCtx::ProfScope ps(&dev, PKV_K_MERGE, st);
     return dev_status(pkv::launch_merge(a, st));
   }
@@ -539,12 +563,12 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (!K_new_dev || !V_new_dev) return PKV_ERR_BAD_ARG;
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
-  const RowDesc* rows = nullptr;
+  const int32_t* rows = nullptr;
   if (pool_rows(pool, seqs, M, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
   const PagedMap pm = make_paged_map(pool, layer);
   DeviceCtx::ProfScope ps(&pool->dev, PKV_K_APPEND, st);
   return dev_status(pkv::launch_append(
-      pm, rows, K_new_dev, V_new_dev, M, n_new,
+      pm, reinterpret_cast<const RowDesc*>(rows), K_new_dev, V_new_dev, M, n_new,
       pool->meta.n_kv_heads() * pool->meta.head_dim(), pool->meta.head_dim(), st));
 }
 
@@ -561,13 +585,11 @@ size_t pkv_decode_workspace_bytes(pkv_pool* pool, const int32_t* seqs,
   if (m.check_batch(seqs, M) != PKV_OK) return static_cast<size_t>(-1);
   if (!pkv::fast_decode_ok(m.head_dim(), n_heads / m.n_kv_heads(), m.block_size()))
     return 0;
-  int32_t items = 0, max_sp = 0;
   std::vector<int32_t> tmp;
-  for (int32_t r = 0; r < M; ++r) {
-    push_row(tmp, m.seq(seqs[r])->seq_len, 0, &items);
-    max_sp = std::max(max_sp, tmp.back());
-  }
-  return partial_bytes(items, max_sp, n_heads, m.head_dim());
+  const RowPlan pl = build_rows(tmp, M, [&](int32_t r) {
+    return std::make_pair(m.seq(seqs[r])->seq_len, 0);
+  });
+  return partial_bytes(pl, n_heads, m.head_dim());
 }
 
 int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
@@ -588,12 +610,12 @@ int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
-  const RowDesc* rows = nullptr;
+  const int32_t* rows = nullptr;
   if (pool_rows(pool, seqs, M, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
   const PagedMap pm = make_paged_map(pool, layer);
-  return run_attention(pool->dev, pm, rows, pool->n_items, pool->max_splits, Q_dev,
-                       out_dev, ws_dev, n_heads, n_kv_heads, head_dim, 1, 1, scale,
-                       M, m.block_size(), true, st);
+  return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, ws_dev,
+                       n_heads, n_kv_heads, head_dim, 1, 1, scale, M,
+                       m.block_size(), true, st);
 }
 
 int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
@@ -612,12 +634,12 @@ int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
-  const RowDesc* rows = nullptr;
+  const int32_t* rows = nullptr;
   if (pool_rows(pool, seqs, M, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
   const PagedMap pm = make_paged_map(pool, layer);
-  return run_attention(pool->dev, pm, rows, pool->n_items, 1, Q_dev, out_dev,
-                       nullptr, n_heads, n_kv_heads, head_dim, n_q,
-                       causal ? 1 : 0, scale, M, m.block_size(), false, st);
+  return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, nullptr,
+                       n_heads, n_kv_heads, head_dim, n_q, causal ? 1 : 0, scale,
+                       M, m.block_size(), false, st);
 }
 
 // ---------------------------------------------------------------- contiguous
@@ -636,21 +658,18 @@ namespace {
 // Rows for contiguous calls (pt_off = slot); checks slots and lengths.
 int32_t contig_rows(const pkv_contig* c, const int32_t* slots,
                     const int32_t* seq_lens, int32_t M, int32_t n,
-                    std::vector<int32_t>& rows, int32_t* n_items,
-                    int32_t* max_splits) {
+                    std::vector<int32_t>& rows, RowPlan* pl) {
   if (!slots || !seq_lens) return PKV_ERR_BAD_ARG;
-  rows.clear();
-  *n_items = 0;
-  *max_splits = 0;
   for (int32_t r = 0; r < M; ++r) {
     if (slots[r] < 0 || slots[r] >= c->n_slots) return PKV_ERR_SEQ;
     for (int32_t r2 = 0; r2 < r; ++r2)
       if (slots[r2] == slots[r]) return PKV_ERR_SEQ;
     if (seq_lens[r] < 0) return PKV_ERR_BAD_ARG;
     if (static_cast<int64_t>(seq_lens[r]) + n > c->max_seq) return PKV_ERR_SEQ;
-    push_row(rows, seq_lens[r], slots[r], n_items);
-    *max_splits = std::max(*max_splits, rows.back());
   }
+  *pl = build_rows(rows, M, [&](int32_t r) {
+    return std::make_pair(seq_lens[r], slots[r]);
+  });
   return PKV_OK;
 }
 
@@ -666,9 +685,8 @@ int32_t pkv_contig_append(const pkv_contig* cache, const int32_t* slots,
   if (!K_new_dev || !V_new_dev) return PKV_ERR_BAD_ARG;
   std::lock_guard<std::mutex> g(contig_mutex());
   std::vector<int32_t> rows;
-  int32_t n_items = 0, max_sp = 0;
-  if (int32_t rc = contig_rows(cache, slots, seq_lens, M, n_new, rows, &n_items, &max_sp))
-    return rc;
+  RowPlan pl;
+  if (int32_t rc = contig_rows(cache, slots, seq_lens, M, n_new, rows, &pl)) return rc;
   DeviceCtx& dev = contig_ctx();
   const hipStream_t st = as_stream(stream);
   if (dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
@@ -688,14 +706,13 @@ size_t pkv_contig_decode_workspace_bytes(const int32_t* seq_lens, int32_t M,
       n_heads % n_kv_heads != 0)
     return static_cast<size_t>(-1);
   if (!pkv::fast_decode_ok(head_dim, n_heads / n_kv_heads, 16)) return 0;
-  int32_t items = 0, max_sp = 0;
-  std::vector<int32_t> tmp;
-  for (int32_t r = 0; r < M; ++r) {
+  for (int32_t r = 0; r < M; ++r)
     if (seq_lens[r] < 0) return static_cast<size_t>(-1);
-    push_row(tmp, seq_lens[r], 0, &items);
-    max_sp = std::max(max_sp, tmp.back());
-  }
-  return partial_bytes(items, max_sp, n_heads, head_dim);
+  std::vector<int32_t> tmp;
+  const RowPlan pl = build_rows(tmp, M, [&](int32_t r) {
+    return std::make_pair(seq_lens[r], 0);
+  });
+  return partial_bytes(pl, n_heads, head_dim);
 }
 
 namespace {
@@ -713,13 +730,12 @@ int32_t contig_attention(const pkv_contig* cache, const int32_t* slots,
   if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
   std::lock_guard<std::mutex> g(contig_mutex());
   std::vector<int32_t> rows;
-  int32_t n_items = 0, max_sp = 0;
-  if (int32_t rc = contig_rows(cache, slots, seq_lens, M, n_q, rows, &n_items, &max_sp))
-    return rc;
+  RowPlan pl;
+  if (int32_t rc = contig_rows(cache, slots, seq_lens, M, n_q, rows, &pl)) return rc;
   const int32_t group = n_heads / n_kv_heads;
   const bool fast = decode && pkv::fast_decode_ok(head_dim, group, cache->block_size);
   if (fast) {
-    const size_t need = partial_bytes(n_items, max_sp, n_heads, head_dim);
+    const size_t need = partial_bytes(pl, n_heads, head_dim);
     if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
   }
   DeviceCtx& dev = contig_ctx();
@@ -728,8 +744,7 @@ int32_t contig_attention(const pkv_contig* cache, const int32_t* slots,
   int32_t* d = nullptr;
   if (dev.upload(kRows, rows, {}, st, &d) != hipSuccess) return PKV_ERR_DEVICE;
   const ContigMap cm = make_contig_map(cache, layer);
-  return run_attention(dev, cm, reinterpret_cast<const RowDesc*>(d), n_items,
-                       decode ? max_sp : 1, Q_dev, out_dev, ws_dev, n_heads,
+  return run_attention(dev, cm, d, pl, Q_dev, out_dev, ws_dev, n_heads,
                        n_kv_heads, head_dim, n_q, causal, scale, M,
                        cache->block_size, decode, st);
 }

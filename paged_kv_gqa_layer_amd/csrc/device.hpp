@@ -5,9 +5,13 @@
 // mirror of every sequence's page table, int32 [max_seqs][stride], kept up
 // to date by small patch lists.  Per call the kernels get one RowDesc per
 // batch row (uploaded once per pool version and batch, so all layers of a
-// step share it).  Decode work items (row, key split) are numbered row by
-// row; the decode kernel finds an item's row by binary search over
-// first_item.
+// step share it).
+//
+// Decode work items: each row's keys are cut into 512-key splits.  Items
+// 0 .. n_full_items-1 are the full splits, numbered row by row (the kernel
+// finds an item's row by binary search over first_full); the remaining
+// items are the rows' partial last splits, longest first (tail_rows), so the
+// end of the grid is filled with the shortest work.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,9 +24,12 @@ struct RowDesc {
   int32_t start;       // rows cached before this call (= seq_len)
   int32_t pt_off;      // paged: offset of the row's page table in the mirror;
                        // contiguous: the cache slot
-  int32_t first_item;  // decode: first split item of this row
-  int32_t n_splits;    // decode: split items of this row (n_q = 1)
+  int32_t first_full;  // decode: first full-split item of this row
+  int32_t n_splits;    // decode: splits of this row (n_q = 1), last may be partial
+  int32_t part_base;   // decode: partial-result slot of split 0
+  int32_t pad[3];
 };
+constexpr int kRowInts = sizeof(RowDesc) / sizeof(int32_t);
 
 // Address of one page (block_size consecutive positions) of one kv head:
 // K rows at the returned pointer, V rows at + v_off; position t of the page
@@ -74,10 +81,12 @@ inline bool fast_prefill_ok(int32_t head_dim, int32_t group, int32_t block) {
 
 struct AttnArgs {
   const RowDesc* rows;
+  const int32_t* tail_rows;  // decode: rows of the partial-split items
   const float* Q;
   float* out;
-  float* part_o;      // [items][n_heads][head_dim]   (decode with splits)
-  float* part_ml;     // [items][n_heads][2]
+  float* part_o;      // [slots][n_heads][head_dim]   (decode with splits)
+  float* part_ml;     // [slots][n_heads][2]
+  int32_t n_full_items;
   int32_t n_rows;
   int32_t n_heads;
   int32_t n_kv_heads;

@@ -160,12 +160,12 @@ __global__ __launch_bounds__(256) void cow_kernel(float* base,
 // weighted sum, which runs over the splits in ascending order.
 // One wave merges one head j of the group.
 __device__ __forceinline__ void merge_head(const AttnArgs& a, int32_t row,
-                                           int32_t head, int32_t first_item,
+                                           int32_t head, int32_t part_base,
                                            int32_t nsp, int lane) {
   constexpr int D = 128;
   constexpr int U = 8;  // split rows loaded together
   const int64_t H = a.n_heads;
-  const int64_t h0 = (int64_t)first_item * H + head;
+  const int64_t h0 = (int64_t)part_base * H + head;
   float mx = kNegInf;
   for (int32_t s = lane; s < nsp; s += 64) mx = fmaxf(mx, a.part_ml[(h0 + s * H) * 2]);
   mx = wave_max(mx);
@@ -212,16 +212,23 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   const int32_t G = a.n_kv_heads;
   const int32_t item_idx = blockIdx.x / G;
   const int32_t kvh = blockIdx.x - item_idx * G;
-  // the row owning this item: last row with first_item <= item_idx
-  int32_t lo = 0, hi = a.n_rows - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (a.rows[mid].first_item <= item_idx) lo = mid; else hi = mid - 1;
+  int32_t row, split;
+  if (item_idx < a.n_full_items) {
+    // full split: the last row with first_full <= item_idx owns it
+    int32_t lo = 0, hi = a.n_rows - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (a.rows[mid].first_full <= item_idx) lo = mid; else hi = mid - 1;
+    }
+    row = lo;
+    split = item_idx - a.rows[row].first_full;
+  } else {
+    row = a.tail_rows[item_idx - a.n_full_items];
+    split = a.rows[row].n_splits - 1;
   }
-  const int32_t row = lo;
   const RowDesc rd = a.rows[row];
-  const int32_t split = item_idx - rd.first_item;
   const int32_t nsp = rd.n_splits;
+  const int32_t slot = rd.part_base + split;
   const int lane = threadIdx.x;
   const int rr = lane >> 4;
   const int c = lane & 15;
@@ -401,7 +408,7 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
       }
     }
   } else {
-    const int64_t hbase = (int64_t)item_idx * a.n_heads + (int64_t)kvh * GROUP;
+    const int64_t hbase = (int64_t)slot * a.n_heads + (int64_t)kvh * GROUP;
 #pragma unroll
     for (int j = 0; j < GROUP; ++j) {
       if ((j & 3) == rr) {
@@ -419,21 +426,18 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   }
 }
 
-// Split merge kernel: one wave per (row, kv head) of a row with splits.  A
-// separate launch (rather than the last split merging in place) keeps the
-// partials coherent across XCDs through the kernel boundary; an in-kernel
-// merge needs a device-scope release per split, which costs more than this
-// launch.
-// One workgroup per row, one wave per query head (block of 256 threads walks
-// the row's heads four at a time).
+// Split merge kernel: one wave per (row, query head) of a row with splits,
+// four heads per workgroup.  A separate launch (rather than the last split
+// merging in place) keeps the partials coherent across XCDs through the
+// kernel boundary; an in-kernel merge needs a device-scope release per split,
+// which costs more than this launch.
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
-  const int32_t row = blockIdx.x;
+  const int32_t quads = (a.n_heads + 3) / 4;
+  const int32_t row = blockIdx.x / quads;
+  const int32_t head = (blockIdx.x - row * quads) * 4 + (threadIdx.x >> 6);
   const RowDesc rd = a.rows[row];
-  if (rd.n_splits <= 1) return;
-  const int w = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  for (int32_t head = w; head < a.n_heads; head += 4)
-    merge_head(a, row, head, rd.first_item, rd.n_splits, lane);
+  if (rd.n_splits <= 1 || head >= a.n_heads) return;
+  merge_head(a, row, head, rd.part_base, rd.n_splits, threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------------------
@@ -777,7 +781,7 @@ hipError_t decode_fast_impl(const Map& m, const AttnArgs& a, int32_t group,
 }
 
 hipError_t merge_impl(const AttnArgs& a, hipStream_t st) {
-  merge_kernel<<<a.n_rows, 256, 0, st>>>(a);
+  merge_kernel<<<a.n_rows * ((a.n_heads + 3) / 4), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
