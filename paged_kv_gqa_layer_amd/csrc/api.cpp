@@ -6,8 +6,8 @@
 //    current by patch lists (one entry per page-table write on the host,
 //    applied by a small kernel before the next kernel that reads the mirror);
 //  - per batch row, one RowDesc (length, mirror offset, decode split range),
-//    uploaded once per pool version and batch, so every layer of a step
-//    reuses the same upload.
+//    uploaded together with the pending patches once per pool version and
+//    batch, so every layer of a step reuses the same upload.
 // Uploads go through a ring of pinned staging slots; a slot is rewritten only
 // after the event recorded behind its previous copy has completed.  All
 // copies and kernels of a pool go to the caller's stream, in call order.
@@ -33,7 +33,7 @@ using pkv::RowDesc;
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr int kStageSlots = 8;
 
-enum Buf { kRows = 0, kPatch = 1, kCow = 2, kNumBufs = 3 };
+enum Buf { kRows = 0, kCow = 1, kNumBufs = 2 };
 
 inline int32_t ceil_div(int64_t a, int64_t b) {
   return static_cast<int32_t>((a + b - 1) / b);
@@ -256,7 +256,7 @@ struct pkv_pool {
   std::vector<int32_t> rows;
   RowPlan plan;
   std::vector<int64_t> rows_key;
-  std::vector<int32_t> scratch;
+  size_t patch_off = 0;  // patches follow the rows in the blob
   std::unordered_set<int64_t> seen;
 
   pkv_pool(int32_t nb, int32_t bs, int32_t nl, int32_t g, int32_t d, int32_t ms)
@@ -269,72 +269,76 @@ struct pkv_pool {
 
 namespace {
 
-// Bring the page-table mirror up to date on `st`: (re)allocate it when a
-// sequence may outgrow its stride, then apply the pending patches.
-hipError_t sync_mirror(pkv_pool* p, hipStream_t st) {
+// (Re)allocate the page-table mirror when a sequence may outgrow its stride;
+// a new mirror is filled from every live page-table entry.
+hipError_t size_mirror(pkv_pool* p, hipStream_t st) {
   auto& m = p->meta;
-  hipError_t e;
   const int64_t need = std::max<int64_t>(m.max_pages_seen(), 1);
-  if (!p->mirror || need > p->stride) {
-    if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
-    if (p->mirror) (void)hipFree(p->mirror);
-    p->mirror = nullptr;
-    const int64_t stride = (need + 63) / 64 * 64;
-    if ((e = hipMalloc(&p->mirror, static_cast<size_t>(m.max_seqs()) * stride *
-                                       sizeof(int32_t))) != hipSuccess)
-      return e;
-    p->stride = stride;
-    p->rows_key.clear();  // row descriptors hold mirror offsets
-    // the new mirror needs every live page-table entry
-    auto& pt = m.patches();
-    pt.clear();
-    for (int32_t s = 0; s < m.max_seqs(); ++s) {
-      const pkv::SeqMeta* q = m.seq(s);
-      if (!q) continue;
-      for (int32_t i = 0; i < static_cast<int32_t>(q->pages.size()); ++i)
-        pt.push_back({s, i, q->pages[i]});
-    }
-  }
+  if (p->mirror && need <= p->stride) return hipSuccess;
+  hipError_t e;
+  if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+  if (p->mirror) (void)hipFree(p->mirror);
+  p->mirror = nullptr;
+  const int64_t stride = (need + 63) / 64 * 64;
+  if ((e = hipMalloc(&p->mirror, static_cast<size_t>(m.max_seqs()) * stride *
+                                     sizeof(int32_t))) != hipSuccess)
+    return e;
+  p->stride = stride;
+  p->rows_key.clear();  // row descriptors hold mirror offsets
   auto& pt = m.patches();
-  if (pt.empty()) return hipSuccess;
-  // The patch kernel writes entries in parallel, so keep only the last write
-  // of each (sequence, page) entry (a fork's share followed by a
-  // copy-on-append replacement, for example).
-  p->scratch.clear();
-  p->seen.clear();
-  for (auto it = pt.rbegin(); it != pt.rend(); ++it) {
-    if (!p->seen.insert(static_cast<int64_t>(it->seq) * p->stride + it->page).second)
-      continue;
-    p->scratch.push_back(it->seq);
-    p->scratch.push_back(it->page);
-    p->scratch.push_back(it->block);
-  }
   pt.clear();
-  int32_t* d = nullptr;
-  if ((e = p->dev.upload(kPatch, p->scratch, {}, st, &d)) != hipSuccess) return e;
-  return pkv::launch_patch(p->mirror, d, static_cast<int32_t>(p->scratch.size() / 3),
-                           p->stride, st);
+  for (int32_t s = 0; s < m.max_seqs(); ++s) {
+    const pkv::SeqMeta* q = m.seq(s);
+    if (!q) continue;
+    for (int32_t i = 0; i < static_cast<int32_t>(q->pages.size()); ++i)
+      pt.push_back({s, i, q->pages[i]});
+  }
+  return hipSuccess;
 }
 
-// Row descriptors of this batch on the device (uploaded unless the device
-// copy already describes this batch at this pool version).
+// Row descriptors of this batch on the device, with the pending page-table
+// patches applied to the mirror first.  Rows and patches travel in one
+// upload, which is skipped when the device copy already describes this batch
+// at this pool version (no patches can be pending then: every page-table
+// change bumps the version).
 hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M,
                      hipStream_t st, const int32_t** rows_dev) {
-  hipError_t e = sync_mirror(p, st);
+  hipError_t e = size_mirror(p, st);
   if (e != hipSuccess) return e;
   std::vector<int64_t> key;
   key.reserve(M + 2);
   key.push_back(static_cast<int64_t>(p->meta.version()));
   key.push_back(p->stride);
   key.insert(key.end(), seqs, seqs + M);
-  if (key != p->rows_key) {
+  auto& pt = p->meta.patches();
+  if (key != p->rows_key || !pt.empty()) {
     p->plan = build_rows(p->rows, M, [&](int32_t r) {
       return std::make_pair(p->meta.seq(seqs[r])->seq_len,
                             static_cast<int32_t>(seqs[r] * p->stride));
     });
+    // The patch kernel writes entries in parallel, so keep only the last
+    // write of each (sequence, page) entry (a fork's share followed by a
+    // copy-on-append replacement, for example).
+    p->patch_off = p->rows.size();
+    p->seen.clear();
+    for (auto it = pt.rbegin(); it != pt.rend(); ++it) {
+      if (!p->seen.insert(static_cast<int64_t>(it->seq) * p->stride + it->page).second)
+        continue;
+      p->rows.push_back(it->seq);
+      p->rows.push_back(it->page);
+      p->rows.push_back(it->block);
+    }
+    p->rows_key.clear();  // the blob below is new
   }
+  const int32_t n_patch = static_cast<int32_t>((p->rows.size() - p->patch_off) / 3);
   int32_t* d = nullptr;
   if ((e = p->dev.upload(kRows, p->rows, key, st, &d)) != hipSuccess) return e;
+  if (!pt.empty()) {
+    pt.clear();
+    if ((e = pkv::launch_patch(p->mirror, d + p->patch_off, n_patch, p->stride, st)) !=
+        hipSuccess)
+      return e;
+  }
   p->rows_key = key;
   *rows_dev = d;
   return hipSuccess;

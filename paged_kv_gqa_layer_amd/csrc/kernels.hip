@@ -576,15 +576,19 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n,
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 template <class Map>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(Map m, AttnArgs a,
+// Two waves per SIMD (two workgroups per CU): the register budget is capped at
+// 256 so one workgroup's MFMAs overlap the other's softmax, LDS and barriers.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_mfma_kernel(Map m, AttnArgs a,
                                                           int32_t n_qt,
                                                           int32_t n_wg) {
   constexpr int D = 128;
   constexpr int KT = 32;
   constexpr int KSTR = 132;  // padded LDS row strides (bank spread)
   constexpr int VSTR = 136;
-  __shared__ float Ks[KT * KSTR];
-  __shared__ float Vs[KT * VSTR];
+  // two K/V tile buffers: tile t+1 is stored while tile t is read
+  __shared__ float Ks2[2][KT * KSTR];
+  __shared__ float Vs2[2][KT * VSTR];
 
   // Keep all query tiles of one (row, kv head) on one XCD (they share K/V).
   const int32_t b = blockIdx.x;
@@ -662,20 +666,22 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(Map m, AttnArgs a,
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int key = ld_key + 8 * u;
-      *reinterpret_cast<float4*>(&Ks[key * KSTR + ld_c]) = kr[u];
-      *reinterpret_cast<float4*>(&Vs[key * VSTR + ld_c]) = vr[u];
+      *reinterpret_cast<float4*>(&Ks2[buf][key * KSTR + ld_c]) = kr[u];
+      *reinterpret_cast<float4*>(&Vs2[buf][key * VSTR + ld_c]) = vr[u];
     }
   };
 
   load_tile(0);
-  store_tile();
+  store_tile(0);
   __syncthreads();
   for (int32_t t = 0; t < n_tiles; ++t) {
     if (t + 1 < n_tiles) load_tile(t + 1);
+    const float* Ks = Ks2[t & 1];
+    const float* Vs = Vs2[t & 1];
     const int32_t k0 = t * KT;
     if (k0 < wkmax) {
       floatx16 S = {};
@@ -727,11 +733,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(Map m, AttnArgs a,
         O3 = __builtin_amdgcn_mfma_f32_32x32x2f32(S[s], vrow[96], O3, 0, 0, 0);
       }
     }
+    // The other buffer was last read in iteration t-1, which ended with a
+    // barrier, so it can be refilled now; one barrier per tile.
+    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
     __syncthreads();
-    if (t + 1 < n_tiles) {
-      store_tile();
-      __syncthreads();
-    }
   }
 
   // normalise and store: accumulator r holds row 8*(r/4) + 4*h + r%4, dim 32*db + lr
