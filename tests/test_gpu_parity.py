@@ -367,3 +367,81 @@ def test_forks_copy_on_append_in_first_step(prefix, n_forks):
     tails = [pool.seq_pages(s)[prefix // 16] for s in forks]
     if prefix % 16:
         assert len(set(tails)) == n_forks
+
+
+def test_multilayer_decode_steps_vs_oracle():
+    """The step protocol over several layers: ensure once, append + attend
+    per layer (each layer with its own K/V and Q), advance once; each layer
+    attends over its own rows only."""
+    H, G, D, L = 32, 8, 128, 3
+    rng = np.random.default_rng(77)
+    lens = [600, 1500, 3, 1023]
+    M = len(lens)
+    pool = pkv.Pool(sum(l // 16 + 4 for l in lens), 16, L, G, D, max_seqs=8)
+    pool.set_free_order(rng.permutation(pool.n_blocks))
+    seqs = [pool.seq_new(l + 8) for l in lens]
+    hist = [[(rng.standard_normal((l, G * D)).astype(np.float32),
+              rng.standard_normal((l, G * D)).astype(np.float32)) for l in lens]
+            for _ in range(L)]
+    for layer in range(L):
+        for r, s in enumerate(seqs):
+            k, v = hist[layer][r]
+            if layer == 0:
+                pool.ensure_append([s], lens[r], check=True)
+            pool.append_layer([s], lens[r], layer, dev(k), dev(v), check=True)
+    pool.advance(seqs, 0, check=False)  # rejected (n <= 0), state unchanged
+    for r, s in enumerate(seqs):
+        pool.advance([s], lens[r], check=True)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    for step in range(3):
+        pool.ensure_append(seqs, 1, check=True)
+        ws = torch.empty(max(pool.decode_workspace_bytes(seqs, H), 4),
+                         dtype=torch.uint8, device="cuda")
+        for layer in range(L):
+            q = rng.standard_normal((M, H * D)).astype(np.float32)
+            k = rng.standard_normal((M, G * D)).astype(np.float32)
+            v = rng.standard_normal((M, G * D)).astype(np.float32)
+            pool.append_layer(seqs, 1, layer, dev(k), dev(v), check=True)
+            out = torch.full((M, H * D), float("nan"), device="cuda")
+            pool.attn_paged_decode(seqs, layer, H, G, D, dev(q), scale, out, ws=ws,
+                                   check=True)
+            torch.cuda.synchronize()
+            got = out.cpu().numpy()
+            for r in range(M):
+                kh, vh = hist[layer][r]
+                kh = np.concatenate([kh, k[r:r + 1]])
+                vh = np.concatenate([vh, v[r:r + 1]])
+                hist[layer][r] = (kh, vh)
+                rc, ref = oracle.attn_contig(q[r:r + 1], kh, vh, H, G, D, True, scale)
+                assert rc == 0
+                assert_close(got[r:r + 1], ref, "step %d layer %d row %d" % (step, layer, r))
+        pool.advance(seqs, 1, check=True)
+
+
+def test_page_table_mirror_grows_after_first_use():
+    """A sequence created after device work has started may need a longer
+    page table than any before it; the mirror is rebuilt and every earlier
+    sequence keeps reading its own rows."""
+    H, G, D = 32, 8, 128
+    rng = np.random.default_rng(78)
+    pool = pkv.Pool(400, 16, 1, G, D, max_seqs=4)
+    pool.set_free_order(rng.permutation(400))
+    a = pool.seq_new(40)
+    ha = (rng.standard_normal((33, G * D)).astype(np.float32),
+          rng.standard_normal((33, G * D)).astype(np.float32))
+    fill_history(pool, [a], lambda r: ha)
+    b = pool.seq_new(5000)  # far longer page table than a's
+    hb = (rng.standard_normal((4100, G * D)).astype(np.float32),
+          rng.standard_normal((4100, G * D)).astype(np.float32))
+    fill_history(pool, [b], lambda r: hb)
+    q = rng.standard_normal((2, H * D)).astype(np.float32)
+    k = rng.standard_normal((2, G * D)).astype(np.float32)
+    v = rng.standard_normal((2, G * D)).astype(np.float32)
+    scale = 0.09
+    out = decode_step(pool, [a, b], q, k, v, H, G, D, scale)
+    got = out.cpu().numpy()
+    for r, h in enumerate((ha, hb)):
+        rc, ref = oracle.attn_contig(q[r:r + 1], np.concatenate([h[0], k[r:r + 1]]),
+                                     np.concatenate([h[1], v[r:r + 1]]), H, G, D, True,
+                                     scale)
+        assert_close(got[r:r + 1], ref, "row %d" % r)
