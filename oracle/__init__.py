@@ -76,6 +76,7 @@ def lib():
             "pkvo_refcounts": (I, [P, P]),
             "pkvo_free_stack": (I, [P, P, I]),
             "pkvo_read_row": (I, [P, I, I, I, P, P]),
+            "pkvo_rope": (I, [P, I, I, I, P, C.c_double]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -113,6 +114,20 @@ def attn_contig(Q, K, V, n_heads, n_kv_heads, head_dim, causal, scale):
     rc = lib().pkvo_attn_contig(_ptr(Q), _ptr(K), _ptr(V), n_q, total_k,
                                 n_heads, n_kv_heads, head_dim, int(causal),
                                 float(scale), _ptr(out))
+    return rc, out
+
+
+def rope(x, n_heads, head_dim, positions, log_base):
+    """Rotary embedding (neox form) of rows x [n, n_heads*head_dim] at the
+    given positions; log_base is ln(rotary base).  Returns (status, rotated
+    copy)."""
+    out = np.array(x, dtype=np.float32, copy=True, order="C")
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32).reshape(-1))
+    n = out.shape[0]
+    if pos.size != n:
+        raise ValueError("one position per row")
+    rc = lib().pkvo_rope(_ptr(out), n, n_heads, head_dim, _ptr(pos),
+                         float(log_base))
     return rc, out
 
 

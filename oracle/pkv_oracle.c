@@ -163,6 +163,53 @@ int pkvo_gqa_attention(const float *Q, const float *K, const float *V,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Rotary position embedding applied before the append and the attention.   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * pkvo_rope -- [P3] (nx_f32_llama_block_forward_v4b, the RoPE step before
+ * attention): when rotary embedding is on, every query head and every kv
+ * head of the new rows is rotated in the "neox" form at the row's position
+ * (the sequence's current length for a decode row, that length + t for
+ * token t of a chunk) before K is appended and Q attends.  The page names
+ * the form and passes a "log base" but does not spell out the rotation; the
+ * reading taken is the standard neox rotary embedding with log_base the
+ * natural logarithm of the rotary base: with half = D / 2 and frequency
+ * inv_i = exp(-(2 i / D) * log_base), the pair (x_i, x_{i+half}) turns by
+ * the angle pos * inv_i,
+ *   x_i'        = x_i cos - x_{i+half} sin
+ *   x_{i+half}' = x_i sin + x_{i+half} cos,
+ * evaluated in double and rounded once to float.  x: [n_rows, n_heads *
+ * head_dim], rotated in place; positions[r] is row r's position (>= 0).
+ */
+int pkvo_rope(float *x, int n_rows, int n_heads, int head_dim,
+              const int *positions, double log_base)
+{
+    if (n_rows <= 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 2 != 0)
+        return O_BAD_DIM;
+    if (!(log_base > 0.0))
+        return O_BAD_ARG;
+    for (int r = 0; r < n_rows; r++)
+        if (positions[r] < 0)
+            return O_BAD_ARG;
+    const int half = head_dim / 2;
+    for (int r = 0; r < n_rows; r++) {
+        for (int h = 0; h < n_heads; h++) {
+            float *v = x + ((size_t)r * n_heads + h) * head_dim;
+            for (int i = 0; i < half; i++) {
+                const double inv = exp(-((double)(2 * i) / head_dim) * log_base);
+                const double ang = (double)positions[r] * inv;
+                const double c = cos(ang), s = sin(ang);
+                const double a = v[i], b = v[i + half];
+                v[i] = (float)(a * c - b * s);
+                v[i + half] = (float)(a * s + b * c);
+            }
+        }
+    }
+    return O_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Contiguous cache: the twin that [P1] and [P4] compare the pool against.   */
 /* ------------------------------------------------------------------------ */
 
