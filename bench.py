@@ -137,7 +137,8 @@ def bench_decode(args, synth, pkv):
     import torch
     mk = synth.decode_m256 if args.workload == "decode_m256" else synth.decode_m32
     n_steps = args.warmup + args.steps
-    wl = mk(max_steps=n_steps + 1)
+    # head-room for the plain run and the rotary run after it
+    wl = mk(max_steps=2 * n_steps + 1)
     H, G, D = wl.n_heads, wl.n_kv_heads, wl.head_dim
     M = wl.M
     log("workload %s: M=%d, cached rows %d..%d (sum %d), pool %d blocks (%.2f GB)"
@@ -160,48 +161,66 @@ def bench_decode(args, synth, pkv):
     out = torch.empty((M, H * D), device="cuda")
     seqs_np = np.asarray(seqs, np.int32)
     # workspace for the longest step (contexts grow by one row per step)
-    wsb = int(sum(math.ceil((int(c) + n_steps + 1) / 512) for c in wl.ctx)) * H * (D + 2) * 4
+    wsb = int(sum(math.ceil((int(c) + 2 * n_steps + 1) / 512) for c in wl.ctx)) * H * (D + 2) * 4
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     scale = wl.scale
 
     def step(t):
-        q, k, v = steps[t]
+        q, k, v = steps[t % n_steps]
         pool.ensure_append(seqs_np, 1, check=True)
         pool.append_layer(seqs_np, 1, 0, k, v, check=True)
         pool.attn_paged_decode(seqs_np, 0, H, G, D, q, scale, out, ws=ws, check=True)
         pool.advance(seqs_np, 1, check=True)
 
-    for t in range(args.warmup):
-        step(t)
-    torch.cuda.synchronize()
-    pool.profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for t in range(args.warmup, n_steps):
-        step(t)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    def run(t_first):
+        """warmup + timed steps from step index t_first (rows cached before
+        step t: ctx + t)."""
+        for t in range(t_first, t_first + args.warmup):
+            step(t)
+        torch.cuda.synchronize()
+        pool.profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(t_first + args.warmup, t_first + n_steps):
+            step(t)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        kv_bytes = 0
+        for t in range(t_first + args.warmup, t_first + n_steps):
+            kv_bytes += int((wl.ctx.astype(np.int64) + t + 1).sum()) * 2 * wl.kv_dim * 4
+        kern = {}
+        for name, kid in (("append", pkv.K_APPEND), ("decode", pkv.K_DECODE),
+                          ("merge", pkv.K_MERGE), ("cow", pkv.K_COW)):
+            ms, n = pool.profile_read(kid)
+            kern[name] = {"launches": n, "avg_us": (1e3 * ms / n) if n else 0.0}
+        pool.profile_enable(False)
+        dec_s = kern["decode"]["avg_us"] * 1e-6 * kern["decode"]["launches"]
+        return {"elapsed": elapsed, "kv_bytes": kv_bytes, "kern": kern,
+                "gbs": kv_bytes / elapsed / 1e9, "achieved": kv_bytes / dec_s / 1e9}
 
-    kv_bytes = 0
-    for t in range(args.warmup, n_steps):
-        kv_bytes += int((wl.ctx.astype(np.int64) + t + 1).sum()) * 2 * wl.kv_dim * 4
-    kern = {}
-    for name, kid in (("append", pkv.K_APPEND), ("decode", pkv.K_DECODE),
-                      ("merge", pkv.K_MERGE), ("cow", pkv.K_COW)):
-        ms, n = pool.profile_read(kid)
-        kern[name] = {"launches": n, "avg_us": (1e3 * ms / n) if n else 0.0}
-    pool.profile_enable(False)
-    dec_s = kern["decode"]["avg_us"] * 1e-6 * kern["decode"]["launches"]
-    achieved = kv_bytes / dec_s / 1e9
-    gbs = kv_bytes / elapsed / 1e9
-    res = {
-        "wl": wl, "pool": pool, "seqs": seqs, "elapsed": elapsed,
-        "kv_bytes": kv_bytes, "gbs": gbs, "achieved": achieved, "kern": kern,
-        "seq_tok_s": M * args.steps / elapsed,
-    }
+    r = run(0)
+    res = dict(r, wl=wl, pool=pool, seqs=seqs,
+               seq_tok_s=M * args.steps / r["elapsed"])
     log("decode: %.3f ms/step, %.0f GB/s step, kernel %.1f us avg -> %.0f GB/s (%.1f%% of peak)"
-        % (1e3 * elapsed / args.steps, gbs, kern["decode"]["avg_us"], achieved,
-           100 * achieved / HBM_PEAK_GBS))
+        % (1e3 * r["elapsed"] / args.steps, r["gbs"], r["kern"]["decode"]["avg_us"],
+           r["achieved"], 100 * r["achieved"] / HBM_PEAK_GBS))
+
+    # The same steps with rotary embedding fused in (K turned in the append
+    # scatter, Q at load in the decode kernel), base 10000.
+    rope = pkv.Rope(D, math.log(10000.0), wl.max_tokens)
+    pool.set_rope(rope)
+    rr = run(n_steps)
+    pool.set_rope(None)
+    res["rope"] = {
+        "ms_per_step": 1e3 * rr["elapsed"] / args.steps,
+        "gbs": rr["gbs"], "kernel_gbs": rr["achieved"],
+        "kernels_us": {k: v["avg_us"] for k, v in rr["kern"].items()},
+        "step_cost_vs_plain": (r["gbs"] / rr["gbs"]) - 1.0,
+        "step": "as the headline step with a rotary table set (neox, base 1e4)",
+    }
+    log("decode + rope: %.3f ms/step, %.0f GB/s step, append %.1f us, decode %.1f us"
+        % (1e3 * rr["elapsed"] / args.steps, rr["gbs"], rr["kern"]["append"]["avg_us"],
+           rr["kern"]["decode"]["avg_us"]))
     return res
 
 
@@ -341,6 +360,7 @@ def main():
         "pct_hbm_peak": 100.0 * d["gbs"] / HBM_PEAK_GBS,
         "kv_bytes_per_step": d["kv_bytes"] / args.steps,
         "kernels_us": {k: v["avg_us"] for k, v in d["kern"].items()},
+        "rope": d["rope"],
         "roofline": {
             "bound": "hbm", "achieved": d["achieved"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": d["achieved"] / HBM_PEAK_GBS,

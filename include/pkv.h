@@ -76,6 +76,7 @@ extern "C" {
 #define PKV_ERR_UNSUPPORTED 8 /* shape outside what the kernels handle      */
 
 typedef struct pkv_pool pkv_pool;
+typedef struct pkv_rope pkv_rope;
 
 /* Human-readable name of a status code (static string). */
 const char *pkv_strerror(int32_t code);
@@ -125,6 +126,40 @@ int32_t pkv_pool_set_free_order(pkv_pool *pool, const int64_t *ids,
                                 int32_t n);
 
 /* ------------------------------------------------------------------------ */
+/* Rotary position embedding                                                 */
+/*                                                                            */
+/* "nx_f32_llama_v4b.nx source", nx_f32_llama_block_forward_v4b, RoPE step:  */
+/* with rotary embedding on, every query head and every kv head of the new   */
+/* rows is turned in the neox form at the row's position -- the sequence's   */
+/* length for a decode row, length + t for token t of a chunk -- before K is */
+/* appended and Q attends.  Here the turn is fused into the kernels: K rows  */
+/* are turned inside pkv_append_layer's scatter (the pool stores turned K),  */
+/* queries at load inside the attention kernels; V is never turned.  Pair    */
+/* (x_i, x_{i + head_dim/2}) turns by pos * exp(-(2 i / head_dim) *          */
+/* log_base) radians (log_base = ln of the rotary base, the page's           */
+/* rope_log_base):                                                           */
+/*   x_i' = x_i cos - x_{i+half} sin,  x_{i+half}' = x_i sin + x_{i+half} cos */
+/* in double, rounded once to float.                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Build the rotary table (cos, sin in double, [max_positions][head_dim / 2],
+ * 8 * head_dim * max_positions bytes) on the current HIP device.  Returns
+ * NULL for head_dim <= 0 or odd, log_base not finite and > 0,
+ * max_positions <= 0, or a HIP failure.  Free with pkv_rope_free once no
+ * pool or contiguous cache that names it has work left in flight. */
+pkv_rope *pkv_rope_new(int32_t head_dim, double log_base,
+                       int32_t max_positions);
+void pkv_rope_free(pkv_rope *rope);
+
+/* Turn rotary embedding on for the pool with this table (borrowed: it must
+ * outlive the pool's use of it), or off with rope == NULL.  It applies to
+ * every later pkv_append_layer (K) and attention call (Q); switch it only
+ * between steps.  Errors: BAD_ARG (pool NULL), BAD_DIM (table head_dim !=
+ * the pool's).  While on, a call whose rows reach position max_positions
+ * or beyond fails with PKV_ERR_CAPACITY before any device work. */
+int32_t pkv_pool_set_rope(pkv_pool *pool, const pkv_rope *rope);
+
+/* ------------------------------------------------------------------------ */
 /* Sequences                                                                 */
 /* ------------------------------------------------------------------------ */
 
@@ -169,7 +204,9 @@ int32_t pkv_ensure_append(pkv_pool *pool, const int32_t *seqs, int32_t M,
  * positions seq_len .. seq_len + n_new - 1 of `layer` for each sequence
  * (one coalesced scatter kernel).  Errors, in this order: BAD_DIM (M or
  * n_new <= 0), SEQ (bad or repeated id), BAD_ARG (layer out of range), SEQ
- * (rows not ensured, or a target block shared), BAD_ARG (NULL pointer).
+ * (rows not ensured, or a target block shared), CAPACITY (rotary table too
+ * short), BAD_ARG (NULL pointer).  With rotary embedding on, K rows are
+ * stored turned at their positions.
  * ("nx_f32_attn_paged.nx source": nx_pkv_append_layer in
  * nx_f32_attn_with_paged, step 1.) */
 int32_t pkv_append_layer(pkv_pool *pool, const int32_t *seqs, int32_t M,
@@ -201,7 +238,9 @@ size_t pkv_decode_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
  * ws_dev: >= pkv_decode_workspace_bytes bytes (may be NULL when that is 0).
  * Errors in the pages' order: BAD_DIM (M, n_heads, n_kv_heads, head_dim
  * <= 0, or head shape != the pool's), BAD_GQA, SEQ, then BAD_ARG (layer,
- * NULL pointer, workspace too small, metadata-only pool), UNSUPPORTED.
+ * metadata-only pool), SEQ (rows not appended), CAPACITY (rotary table too
+ * short), BAD_ARG (NULL pointer, workspace too small), UNSUPPORTED.  With
+ * rotary embedding on, each query is turned at position seq_len (+ i).
  * ("nx_f32_llama_v4b.nx source": per-row nx_f32_attn_with_paged with n_q = 1
  * and causal = 1; "nx_f32_attn_paged.nx source": the attention body.) */
 int32_t pkv_attn_paged_decode(pkv_pool *pool, const int32_t *seqs, int32_t M,
@@ -245,6 +284,9 @@ typedef struct pkv_contig {
     int32_t head_dim;
     int32_t block_size; /* rows per page the kernels iterate by: give the
                            paged pool's block size to get identical bits */
+    const pkv_rope *rope; /* rotary table as pkv_pool_set_rope, or NULL;
+                             its head_dim must equal head_dim (else
+                             PKV_ERR_BAD_ARG) */
 } pkv_contig;
 
 /* Bytes of the contiguous cache above (0 on bad sizes). */

@@ -21,7 +21,7 @@ from ._lib import (BAD_ARG, BAD_DIM, BAD_GQA, CAPACITY, DEVICE, ERR_SEQ,
                    SIZE_MAX, UNSUPPORTED, Contig, PKVError)
 
 __all__ = [
-    "Pool", "ContigCache", "PKVError", "lib", "pool_storage_bytes",
+    "Pool", "ContigCache", "Rope", "PKVError", "lib", "pool_storage_bytes",
     "OK", "BAD_DIM", "BAD_GQA", "ERR_SEQ", "OOM", "CAPACITY", "BAD_ARG",
     "DEVICE", "UNSUPPORTED", "K_APPEND", "K_DECODE", "K_MERGE", "K_PREFILL",
     "K_COW",
@@ -78,6 +78,28 @@ def pool_storage_bytes(n_blocks, block_size, n_layers, n_kv_heads, head_dim):
                                         n_kv_heads, head_dim)
 
 
+class Rope:
+    """Rotary table (``pkv_rope``) on the current GPU: neox-form turns at
+    positions [0, max_positions); ``log_base`` = ln(rotary base)."""
+
+    def __init__(self, head_dim, log_base, max_positions):
+        self.head_dim = head_dim
+        self.log_base = float(log_base)
+        self.max_positions = max_positions
+        self._free = lib().pkv_rope_free  # kept for interpreter shutdown
+        self._h = lib().pkv_rope_new(head_dim, self.log_base, max_positions)
+        if not self._h:
+            raise ValueError("pkv_rope_new failed (bad arguments or HIP error)")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._free(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
 class Pool:
     """A refcounted paged KV pool (``pkv_pool``).
 
@@ -108,6 +130,16 @@ class Pool:
                                      head_dim, max_seqs, ptr, nbytes)
         if not self._h:
             raise ValueError("pkv_pool_new failed (bad sizes)")
+        self.rope = None
+
+    def set_rope(self, rope, check=True):
+        """Turn rotary embedding on with a :class:`Rope` table, or off (None);
+        the pool keeps a reference to the table."""
+        rc = _check(lib().pkv_pool_set_rope(self._h, rope._h if rope else None),
+                    "pool_set_rope", check)
+        if rc == OK:
+            self.rope = rope
+        return rc
 
     def close(self):
         if getattr(self, "_h", None):
@@ -235,15 +267,17 @@ class ContigCache:
     (``pkv_contig``): [n_slots][n_layers][2][n_kv_heads][max_seq][head_dim]."""
 
     def __init__(self, n_slots, n_layers, n_kv_heads, max_seq, head_dim,
-                 block_size=16, device="cuda"):
+                 block_size=16, device="cuda", rope=None):
         import torch
         nbytes = lib().pkv_contig_bytes(n_slots, n_layers, n_kv_heads, max_seq,
                                         head_dim)
         if nbytes == 0:
             raise ValueError("bad cache dims")
         self.buf = torch.zeros(nbytes // 4, dtype=torch.float32, device=device)
+        self.rope = rope  # keeps the table alive
         self.desc = Contig(self.buf.data_ptr(), n_slots, n_layers, n_kv_heads,
-                           max_seq, head_dim, block_size)
+                           max_seq, head_dim, block_size,
+                           rope._h if rope is not None else None)
         self.n_kv_heads = n_kv_heads
         self.head_dim = head_dim
 

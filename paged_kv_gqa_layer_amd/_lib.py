@@ -31,7 +31,7 @@ class Contig(C.Structure):
     _fields_ = [("base_dev", C.c_void_p), ("n_slots", C.c_int32),
                 ("n_layers", C.c_int32), ("n_kv_heads", C.c_int32),
                 ("max_seq", C.c_int32), ("head_dim", C.c_int32),
-                ("block_size", C.c_int32)]
+                ("block_size", C.c_int32), ("rope", C.c_void_p)]
 
 
 _P, _I32, _I64, _F, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
@@ -42,6 +42,9 @@ SIGNATURES = {
     "pkv_pool_storage_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pkv_pool_new": (_P, [_I32, _I32, _I32, _I32, _I32, _I32, _P, _SZ]),
     "pkv_pool_free": (None, [_P]),
+    "pkv_rope_new": (_P, [_I32, C.c_double, _I32]),
+    "pkv_rope_free": (None, [_P]),
+    "pkv_pool_set_rope": (_I32, [_P, _P]),
     "pkv_alloc_block": (_I64, [_P]),
     "pkv_unref_block": (_I32, [_P, _I64]),
     "pkv_pool_set_free_order": (_I32, [_P, _P, _I32]),

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <unordered_set>
@@ -244,6 +245,17 @@ RowPlan build_rows(std::vector<int32_t>& v, int32_t M, F rowinfo) {
 
 // ---------------------------------------------------------------------------
 
+// Rotary table on the device: (cos, sin) in double per (position, pair).
+struct pkv_rope {
+  int32_t head_dim = 0;
+  int32_t max_positions = 0;
+  double log_base = 0.0;
+  double2* table = nullptr;  // [max_positions][head_dim / 2]
+  ~pkv_rope() {
+    if (table) (void)hipFree(table);
+  }
+};
+
 struct pkv_pool {
   pkv::PoolMeta meta;
   float* storage = nullptr;
@@ -258,6 +270,7 @@ struct pkv_pool {
   std::vector<int64_t> rows_key;
   size_t patch_off = 0;  // patches follow the rows in the blob
   std::unordered_set<int64_t> seen;
+  const pkv_rope* rope = nullptr;  // borrowed; null = no rotary embedding
 
   pkv_pool(int32_t nb, int32_t bs, int32_t nl, int32_t g, int32_t d, int32_t ms)
       : meta(nb, bs, nl, g, d, ms) {}
@@ -361,7 +374,7 @@ PagedMap make_paged_map(const pkv_pool* p, int32_t layer) {
 bool contig_valid(const pkv_contig* c) {
   return c && c->base_dev && c->n_slots > 0 && c->n_layers > 0 &&
          c->n_kv_heads > 0 && c->max_seq > 0 && c->head_dim > 0 &&
-         c->block_size > 0;
+         c->block_size > 0 && (!c->rope || c->rope->head_dim == c->head_dim);
 }
 
 ContigMap make_contig_map(const pkv_contig* c, int32_t layer) {
@@ -390,7 +403,8 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
                       const RowPlan& pl, const float* Q, float* out, void* ws,
                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                       int32_t n_q, int32_t causal, float scale, int32_t M,
-                      int32_t block_size, bool decode, hipStream_t st) {
+                      int32_t block_size, bool decode, const double2* rope,
+                      hipStream_t st) {
   const int32_t group = n_heads / n_kv_heads;
   AttnArgs a;
   a.rows = reinterpret_cast<const RowDesc*>(rows_dev);
@@ -410,6 +424,7 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   a.causal = causal;
   a.qscale = static_cast<float>(static_cast<double>(scale) * kLog2e);
   a.n_items = pl.n_items;
+  a.rope = rope;
   hipError_t e;
   if (decode && pkv::fast_decode_ok(head_dim, group, block_size)) {
     {
@@ -431,6 +446,20 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   DeviceCtx::ProfScope ps(&dev, decode ? PKV_K_DECODE : PKV_K_PREFILL, st);
   return dev_status(pkv::launch_generic(map, a, group, st));
 }
+
+// Rows of a call sit at positions seq_len .. seq_len + n - 1; with rotary
+// embedding on, every one must have a row in the table.
+int32_t pool_rope_check(const pkv_pool* p, const int32_t* seqs, int32_t M,
+                        int32_t n) {
+  if (!p->rope) return PKV_OK;
+  for (int32_t r = 0; r < M; ++r)
+    if (static_cast<int64_t>(p->meta.seq(seqs[r])->seq_len) + n >
+        p->rope->max_positions)
+      return PKV_ERR_CAPACITY;
+  return PKV_OK;
+}
+
+const double2* rope_table(const pkv_rope* r) { return r ? r->table : nullptr; }
 
 // Common front checks of the attention calls, in the pages' order.
 int32_t attn_front_checks(int32_t M, int32_t n_q, int32_t n_heads,
@@ -496,6 +525,52 @@ pkv_pool* pkv_pool_new(int32_t n_blocks, int32_t block_size, int32_t n_layers,
 }
 
 void pkv_pool_free(pkv_pool* pool) { delete pool; }
+
+pkv_rope* pkv_rope_new(int32_t head_dim, double log_base,
+                       int32_t max_positions) {
+  if (head_dim <= 0 || head_dim % 2 != 0 || !(log_base > 0.0) ||
+      !std::isfinite(log_base) || max_positions <= 0)
+    return nullptr;
+  const int32_t half = head_dim / 2;
+  // angle of pair i at position p: p * exp(-(2i / head_dim) * log_base)
+  std::vector<double> inv(half);
+  for (int32_t i = 0; i < half; ++i)
+    inv[i] = std::exp(-(static_cast<double>(2 * i) / head_dim) * log_base);
+  std::vector<double> host(static_cast<size_t>(max_positions) * half * 2);
+  for (int32_t p = 0; p < max_positions; ++p) {
+    double* row = host.data() + static_cast<size_t>(p) * half * 2;
+    for (int32_t i = 0; i < half; ++i) {
+      const double ang = static_cast<double>(p) * inv[i];
+      row[2 * i] = std::cos(ang);
+      row[2 * i + 1] = std::sin(ang);
+    }
+  }
+  pkv_rope* r = new (std::nothrow) pkv_rope();
+  if (!r) return nullptr;
+  r->head_dim = head_dim;
+  r->max_positions = max_positions;
+  r->log_base = log_base;
+  const size_t bytes = host.size() * sizeof(double);
+  if (hipMalloc(&r->table, bytes) != hipSuccess) {
+    r->table = nullptr;
+    delete r;
+    return nullptr;
+  }
+  if (hipMemcpy(r->table, host.data(), bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    delete r;
+    return nullptr;
+  }
+  return r;
+}
+
+void pkv_rope_free(pkv_rope* rope) { delete rope; }
+
+int32_t pkv_pool_set_rope(pkv_pool* pool, const pkv_rope* rope) {
+  if (!pool) return PKV_ERR_BAD_ARG;
+  if (rope && rope->head_dim != pool->meta.head_dim()) return PKV_ERR_BAD_DIM;
+  pool->rope = rope;
+  return PKV_OK;
+}
 
 int64_t pkv_alloc_block(pkv_pool* pool) {
   if (!pool) return -1;
@@ -563,6 +638,7 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (int32_t rc = pool->meta.check_batch(seqs, M)) return rc;
   if (layer < 0 || layer >= pool->meta.n_layers()) return PKV_ERR_BAD_ARG;
   if (int32_t rc = pool->meta.check_append(seqs, M, n_new)) return rc;
+  if (int32_t rc = pool_rope_check(pool, seqs, M, n_new)) return rc;
   if (!pool->storage) return PKV_OK;  // metadata-only pool: checks only
   if (!K_new_dev || !V_new_dev) return PKV_ERR_BAD_ARG;
   const hipStream_t st = as_stream(stream);
@@ -573,7 +649,8 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   DeviceCtx::ProfScope ps(&pool->dev, PKV_K_APPEND, st);
   return dev_status(pkv::launch_append(
       pm, reinterpret_cast<const RowDesc*>(rows), K_new_dev, V_new_dev, M, n_new,
-      pool->meta.n_kv_heads() * pool->meta.head_dim(), pool->meta.head_dim(), st));
+      pool->meta.n_kv_heads() * pool->meta.head_dim(), pool->meta.head_dim(),
+      rope_table(pool->rope), st));
 }
 
 int32_t pkv_advance(pkv_pool* pool, const int32_t* seqs, int32_t M, int32_t n) {
@@ -609,6 +686,7 @@ int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (layer < 0 || layer >= m.n_layers()) return PKV_ERR_BAD_ARG;
   if (!pool->storage) return PKV_ERR_BAD_ARG;
   if (int32_t rc = m.check_rows(seqs, M, 1)) return rc;
+  if (int32_t rc = pool_rope_check(pool, seqs, M, 1)) return rc;
   if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
   const size_t need = pkv_decode_workspace_bytes(pool, seqs, M, n_heads);
   if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
@@ -619,7 +697,7 @@ int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
   const PagedMap pm = make_paged_map(pool, layer);
   return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, ws_dev,
                        n_heads, n_kv_heads, head_dim, 1, 1, scale, M,
-                       m.block_size(), true, st);
+                       m.block_size(), true, rope_table(pool->rope), st);
 }
 
 int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
@@ -635,6 +713,7 @@ int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (layer < 0 || layer >= m.n_layers()) return PKV_ERR_BAD_ARG;
   if (!pool->storage) return PKV_ERR_BAD_ARG;
   if (int32_t rc = m.check_rows(seqs, M, n_q)) return rc;
+  if (int32_t rc = pool_rope_check(pool, seqs, M, n_q)) return rc;
   if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
@@ -643,7 +722,7 @@ int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
   const PagedMap pm = make_paged_map(pool, layer);
   return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, nullptr,
                        n_heads, n_kv_heads, head_dim, n_q, causal ? 1 : 0, scale,
-                       M, m.block_size(), false, st);
+                       M, m.block_size(), false, rope_table(pool->rope), st);
 }
 
 // ---------------------------------------------------------------- contiguous
@@ -670,6 +749,8 @@ int32_t contig_rows(const pkv_contig* c, const int32_t* slots,
       if (slots[r2] == slots[r]) return PKV_ERR_SEQ;
     if (seq_lens[r] < 0) return PKV_ERR_BAD_ARG;
     if (static_cast<int64_t>(seq_lens[r]) + n > c->max_seq) return PKV_ERR_SEQ;
+    if (c->rope && static_cast<int64_t>(seq_lens[r]) + n > c->rope->max_positions)
+      return PKV_ERR_CAPACITY;
   }
   *pl = build_rows(rows, M, [&](int32_t r) {
     return std::make_pair(seq_lens[r], slots[r]);
@@ -700,7 +781,8 @@ int32_t pkv_contig_append(const pkv_contig* cache, const int32_t* slots,
   return dev_status(pkv::launch_append(cm, reinterpret_cast<const RowDesc*>(d),
                                        K_new_dev, V_new_dev, M, n_new,
                                        cache->n_kv_heads * cache->head_dim,
-                                       cache->head_dim, st));
+                                       cache->head_dim, rope_table(cache->rope),
+                                       st));
 }
 
 size_t pkv_contig_decode_workspace_bytes(const int32_t* seq_lens, int32_t M,
@@ -750,7 +832,7 @@ int32_t contig_attention(const pkv_contig* cache, const int32_t* slots,
   const ContigMap cm = make_contig_map(cache, layer);
   return run_attention(dev, cm, d, pl, Q_dev, out_dev, ws_dev, n_heads,
                        n_kv_heads, head_dim, n_q, causal, scale, M,
-                       cache->block_size, decode, st);
+                       cache->block_size, decode, rope_table(cache->rope), st);
 }
 
 }  // namespace

@@ -95,18 +95,25 @@ struct AttnArgs {
   int32_t causal;
   float qscale;  // scale * log2(e): scores are kept in base-2 units
   int32_t n_items;
+  // rotary table [positions][head_dim/2] of (cos, sin), or null: queries are
+  // turned at their positions before the scores
+  const double2* rope;
 };
 
 // Launchers (kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_patch(int32_t* mirror, const int32_t* patches, int32_t n,
                         int64_t stride, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
+// rope: rotary table (as AttnArgs::rope) or null; K rows are turned at
+// their positions before they are stored.
 hipError_t launch_append(const PagedMap& m, const RowDesc* rows,
                          const float* K, const float* V, int32_t M, int32_t n,
-                         int32_t kv_dim, int32_t head_dim, hipStream_t st);
+                         int32_t kv_dim, int32_t head_dim, const double2* rope,
+                         hipStream_t st);
 hipError_t launch_append(const ContigMap& m, const RowDesc* rows,
                          const float* K, const float* V, int32_t M, int32_t n,
-                         int32_t kv_dim, int32_t head_dim, hipStream_t st);
+                         int32_t kv_dim, int32_t head_dim, const double2* rope,
+                         hipStream_t st);
 hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,
                       int64_t block_floats, hipStream_t st);
 hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,

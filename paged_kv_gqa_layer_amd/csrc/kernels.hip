@@ -85,16 +85,32 @@ __device__ __forceinline__ float dot8(const float4& ka, const float4& kb,
   return s;
 }
 
+// Rotary embedding, neox form ("nx_f32_llama_v4b.nx source",
+// nx_f32_llama_block_forward_v4b, RoPE step): dims i and i + head_dim/2 of a
+// head turn together by the angle of (position, i).  cs is the rotary table,
+// [positions][head_dim/2] pairs (cos, sin) in double; the rotation runs in
+// double and rounds once to float.
+__device__ __forceinline__ void rotate_pair(float& lo, float& hi,
+                                            const double2 cs) {
+  const double a = lo, b = hi;
+  lo = static_cast<float>(a * cs.x - b * cs.y);
+  hi = static_cast<float>(a * cs.y + b * cs.x);
+}
+
 // ---------------------------------------------------------------------------
 // Append: scatter new K/V rows to their (page, slot).  One thread per VEC
 // floats; a row of one kv head is head_dim contiguous floats on both sides.
+// With rotary embedding (ROPE), a thread takes VEC floats of the first half
+// of a head and the VEC floats they pair with in the second half, and turns
+// the K pairs by the row's position before storing them (V is stored as is).
 // ---------------------------------------------------------------------------
-template <int VEC, class Map>
+template <int VEC, class Map, bool ROPE>
 __global__ __launch_bounds__(256) void append_kernel(
     Map m, const RowDesc* __restrict__ rows, const float* __restrict__ K,
     const float* __restrict__ V, int32_t n, int32_t kv_dim, int32_t head_dim,
-    int64_t total) {
-  const int32_t per_row = kv_dim / VEC;
+    int64_t total, const double2* __restrict__ cs) {
+  const int32_t span = ROPE ? head_dim / 2 : head_dim;  // floats per head unit
+  const int32_t per_row = (ROPE ? kv_dim / 2 : kv_dim) / VEC;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t rt = e / per_row;
@@ -103,12 +119,43 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int32_t t = static_cast<int32_t>(rt - (int64_t)r * n);
     const RowDesc rd = rows[r];
     const int32_t pos = rd.start + t;
-    const int32_t kvh = c / head_dim;
-    const int32_t d = c - kvh * head_dim;
+    const int32_t kvh = c / span;
+    const int32_t d = c - kvh * span;
     float* dst = m.page(rd, pos / m.block_size, kvh) +
                  (int64_t)(pos % m.block_size) * head_dim + d;
-    const int64_t src = rt * kv_dim + c;
-    if constexpr (VEC == 4) {
+    const int64_t src = rt * kv_dim + (int64_t)kvh * head_dim + d;
+    if constexpr (ROPE) {
+      const int32_t half = span;
+      const double2* cr = cs + (int64_t)pos * half + d;
+      float klo[VEC], khi[VEC], vlo[VEC], vhi[VEC];
+      if constexpr (VEC == 4) {
+        const float4 a = ld4(K + src), b = ld4(K + src + half);
+        const float4 va = ld4(V + src), vb = ld4(V + src + half);
+        klo[0] = a.x; klo[1] = a.y; klo[2] = a.z; klo[3] = a.w;
+        khi[0] = b.x; khi[1] = b.y; khi[2] = b.z; khi[3] = b.w;
+        vlo[0] = va.x; vlo[1] = va.y; vlo[2] = va.z; vlo[3] = va.w;
+        vhi[0] = vb.x; vhi[1] = vb.y; vhi[2] = vb.z; vhi[3] = vb.w;
+      } else {
+        klo[0] = K[src];
+        khi[0] = K[src + half];
+        vlo[0] = V[src];
+        vhi[0] = V[src + half];
+      }
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) rotate_pair(klo[j], khi[j], cr[j]);
+      if constexpr (VEC == 4) {
+        *reinterpret_cast<float4*>(dst) = make_float4(klo[0], klo[1], klo[2], klo[3]);
+        *reinterpret_cast<float4*>(dst + half) = make_float4(khi[0], khi[1], khi[2], khi[3]);
+        *reinterpret_cast<float4*>(dst + m.v_off) = make_float4(vlo[0], vlo[1], vlo[2], vlo[3]);
+        *reinterpret_cast<float4*>(dst + m.v_off + half) =
+            make_float4(vhi[0], vhi[1], vhi[2], vhi[3]);
+      } else {
+        dst[0] = klo[0];
+        dst[half] = khi[0];
+        dst[m.v_off] = vlo[0];
+        dst[m.v_off + half] = vhi[0];
+      }
+    } else if constexpr (VEC == 4) {
       *reinterpret_cast<float4*>(dst) = ld4(K + src);
       *reinterpret_cast<float4*>(dst + m.v_off) = ld4(V + src);
     } else {
@@ -247,15 +294,33 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
     for (int j = 0; j < GROUP; ++j) {
       const float4 x = ld4(qrow + j * D + 4 * c);
       const float4 y = ld4(qrow + j * D + 64 + 4 * c);
-      qa[j][0] = x.x * a.qscale;
-      qa[j][1] = x.y * a.qscale;
-      qa[j][2] = x.z * a.qscale;
-      qa[j][3] = x.w * a.qscale;
-      qb[j][0] = y.x * a.qscale;
-      qb[j][1] = y.y * a.qscale;
-      qb[j][2] = y.z * a.qscale;
-      qb[j][3] = y.w * a.qscale;
+      qa[j][0] = x.x;
+      qa[j][1] = x.y;
+      qa[j][2] = x.z;
+      qa[j][3] = x.w;
+      qb[j][0] = y.x;
+      qb[j][1] = y.y;
+      qb[j][2] = y.z;
+      qb[j][3] = y.w;
     }
+    if (a.rope) {
+      // the query sits at position total_k - 1; dims 4c+e pair with 64+4c+e
+      const double2* cr = a.rope + (int64_t)(total_k - 1) * (D / 2) + 4 * c;
+      double2 cse[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cse[e] = cr[e];
+#pragma unroll
+      for (int j = 0; j < GROUP; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rotate_pair(qa[j][e], qb[j][e], cse[e]);
+    }
+#pragma unroll
+    for (int j = 0; j < GROUP; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qa[j][e] *= a.qscale;
+        qb[j][e] *= a.qscale;
+      }
   }
 
   float mrun[GROUP], lrun[GROUP];
@@ -471,8 +536,18 @@ __global__ __launch_bounds__(64) void generic_kernel(Map m, AttnArgs a,
   const int64_t out_row = item_idx;
 
   const float* qrow = a.Q + (out_row * a.n_heads + (int64_t)kvh * group) * D;
+  const int32_t half = D / 2;
   for (int32_t e = lane; e < group * D; e += 64) {
-    q_sh[e] = qrow[e] * a.qscale;
+    float x = qrow[e];
+    if (a.rope) {
+      // rotate the pair (i, i + half) this element belongs to at q_pos
+      const int32_t d = e % D;
+      const int32_t i = d < half ? d : d - half;
+      float lo = qrow[e - d + i], hi = qrow[e - d + i + half];
+      rotate_pair(lo, hi, a.rope[(int64_t)q_pos * half + i]);
+      x = d < half ? lo : hi;
+    }
+    q_sh[e] = x * a.qscale;
     o_sh[e] = 0.f;
   }
   __syncthreads();
@@ -621,13 +696,26 @@ void prefill_mfma_kernel(Map m, AttnArgs a,
         (((int64_t)row * n_q + (row_valid ? qi : 0)) * a.n_heads + kvh * 4 + jh) * D +
         4 * h;
 #pragma unroll
+    for (int t = 0; t < 16; ++t)
+      qreg[t] = row_valid ? ld4(qp + 8 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (a.rope) {
+      // qreg[t] holds dims 8t+4h .. 8t+4h+3; for t < 8 they pair with
+      // qreg[t + 8] (dims + 64).  Rows past n_q hold zeros and stay zero.
+      const double2* cr = a.rope + (int64_t)q_pos * (D / 2) + 4 * h;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        rotate_pair(qreg[t].x, qreg[t + 8].x, cr[8 * t + 0]);
+        rotate_pair(qreg[t].y, qreg[t + 8].y, cr[8 * t + 1]);
+        rotate_pair(qreg[t].z, qreg[t + 8].z, cr[8 * t + 2]);
+        rotate_pair(qreg[t].w, qreg[t + 8].w, cr[8 * t + 3]);
+      }
+    }
+#pragma unroll
     for (int t = 0; t < 16; ++t) {
-      float4 x = row_valid ? ld4(qp + 8 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
-      x.x *= a.qscale;
-      x.y *= a.qscale;
-      x.z *= a.qscale;
-      x.w *= a.qscale;
-      qreg[t] = x;
+      qreg[t].x *= a.qscale;
+      qreg[t].y *= a.qscale;
+      qreg[t].z *= a.qscale;
+      qreg[t].w *= a.qscale;
     }
   }
 
@@ -759,15 +847,26 @@ void prefill_mfma_kernel(Map m, AttnArgs a,
 template <class Map>
 hipError_t append_impl(const Map& m, const RowDesc* rows, const float* K,
                        const float* V, int32_t M, int32_t n, int32_t kv_dim,
-                       int32_t head_dim, hipStream_t st) {
-  const bool vec = (head_dim % 4 == 0);
-  const int64_t total = (int64_t)M * n * kv_dim / (vec ? 4 : 1);
+                       int32_t head_dim, const double2* cs, hipStream_t st) {
+  const bool rope = cs != nullptr;
+  if (rope && head_dim % 2 != 0) return hipErrorInvalidValue;
+  const int32_t span = rope ? head_dim / 2 : head_dim;
+  const bool vec = (span % 4 == 0);
+  const int64_t total = (int64_t)M * n * (rope ? kv_dim / 2 : kv_dim) / (vec ? 4 : 1);
   const int64_t want = (total + 255) / 256;
   const int grid = static_cast<int>(want < 65536 ? (want > 0 ? want : 1) : 65536);
-  if (vec)
-    append_kernel<4, Map><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim, head_dim, total);
+  if (rope && vec)
+    append_kernel<4, Map, true><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
+                                                      head_dim, total, cs);
+  else if (rope)
+    append_kernel<1, Map, true><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
+                                                      head_dim, total, cs);
+  else if (vec)
+    append_kernel<4, Map, false><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
+                                                       head_dim, total, cs);
   else
-    append_kernel<1, Map><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim, head_dim, total);
+    append_kernel<1, Map, false><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
+                                                       head_dim, total, cs);
   return hipGetLastError();
 }
 
@@ -826,13 +925,14 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
 
 hipError_t launch_append(const PagedMap& m, const RowDesc* rows, const float* K,
                          const float* V, int32_t M, int32_t n, int32_t kv_dim,
-                         int32_t head_dim, hipStream_t st) {
-  return append_impl(m, rows, K, V, M, n, kv_dim, head_dim, st);
+                         int32_t head_dim, const double2* rope, hipStream_t st) {
+  return append_impl(m, rows, K, V, M, n, kv_dim, head_dim, rope, st);
 }
 hipError_t launch_append(const ContigMap& m, const RowDesc* rows,
                          const float* K, const float* V, int32_t M, int32_t n,
-                         int32_t kv_dim, int32_t head_dim, hipStream_t st) {
-  return append_impl(m, rows, K, V, M, n, kv_dim, head_dim, st);
+                         int32_t kv_dim, int32_t head_dim, const double2* rope,
+                         hipStream_t st) {
+  return append_impl(m, rows, K, V, M, n, kv_dim, head_dim, rope, st);
 }
 
 hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,

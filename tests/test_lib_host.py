@@ -175,3 +175,20 @@ def test_attention_front_checks_order():
     pre = L.pkv_attn_paged_prefill
     assert pre(p._h, sp, 1, 0, 0, 4, 2, 4, None, 1, 1.0, None, None) == pkv.BAD_DIM
     assert pre(p._h, sp, 1, 2, 0, 6, 4, 4, None, 1, 1.0, None, None) == pkv.BAD_GQA
+
+
+def test_rope_table_argument_checks():
+    """pkv_rope_new refuses bad shapes before touching the device;
+    pkv_pool_set_rope(NULL) switches rotary embedding off on any pool."""
+    L = pkv.lib()
+    assert not L.pkv_rope_new(0, 9.2, 16)
+    assert not L.pkv_rope_new(7, 9.2, 16)       # odd head_dim: no pairs
+    assert not L.pkv_rope_new(8, 0.0, 16)
+    assert not L.pkv_rope_new(8, -1.0, 16)
+    assert not L.pkv_rope_new(8, float("inf"), 16)
+    assert not L.pkv_rope_new(8, float("nan"), 16)
+    assert not L.pkv_rope_new(8, 9.2, 0)
+    L.pkv_rope_free(None)
+    p = pkv.Pool(4, 4, 1, 1, 4, device=None)
+    assert L.pkv_pool_set_rope(p._h, None) == pkv.OK
+    assert L.pkv_pool_set_rope(None, None) == pkv.BAD_ARG
