@@ -249,6 +249,31 @@ int32_t pkv_attn_paged_decode(pkv_pool *pool, const int32_t *seqs, int32_t M,
                               const float *Q_dev, float scale, float *out_dev,
                               void *ws_dev, size_t ws_bytes, void *stream);
 
+/* Device workspace bytes pkv_attn_paged_verify needs for n_q queries per
+ * sequence (split partial results); 0 if none, (size_t)-1 on bad arguments. */
+size_t pkv_verify_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
+                                  int32_t M, int32_t n_q, int32_t n_heads);
+
+/* Multi-query decode: n_q new rows per sequence (appended, not advanced),
+ * offset-causal -- query i sits at position seq_len + i and sees keys
+ * 0 .. seq_len + i -- e.g. verifying n_q drafted tokens in one step, after
+ * which pkv_seq_truncate rewinds the rejected ones ("nx_paged_kv_gate.nx
+ * source": header, "truncate unref" as the speculative-decode rewind; the
+ * result is the prefill's, "nx_f32_attn_paged.nx source" header comment).
+ * Q_dev, out_dev: [M * n_q, n_heads * head_dim], row r * n_q + i.  Keys are
+ * cut into the decode's fixed 512-row splits, merged in a fixed order, so
+ * each output depends only on its own sequence.  Split kernel when
+ * n_q * (n_heads / n_kv_heads) <= 32 with head_dim 128 and 16-row pages
+ * (n_q == 1 runs pkv_attn_paged_decode's kernels, bit for bit); other shapes
+ * run the prefill kernels and need no workspace.  ws_dev: >=
+ * pkv_verify_workspace_bytes bytes.  Errors as pkv_attn_paged_decode plus
+ * BAD_DIM for n_q <= 0. */
+int32_t pkv_attn_paged_verify(pkv_pool *pool, const int32_t *seqs, int32_t M,
+                              int32_t n_q, int32_t layer, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t head_dim,
+                              const float *Q_dev, float scale, float *out_dev,
+                              void *ws_dev, size_t ws_bytes, void *stream);
+
 /* Chunked prefill: n_q new rows per sequence (appended, not advanced),
  * total_k = seq_len + n_q; with causal != 0 query i sees keys
  * 0 .. total_k - n_q + i, otherwise all total_k keys.  Q_dev, out_dev:
@@ -315,6 +340,20 @@ int32_t pkv_attn_contig_decode(const pkv_contig *cache, const int32_t *slots,
                                const float *Q_dev, float scale, float *out_dev,
                                void *ws_dev, size_t ws_bytes, void *stream);
 
+/* Workspace for pkv_attn_contig_verify given per-row seq_lens. */
+size_t pkv_contig_verify_workspace_bytes(const int32_t *seq_lens, int32_t M,
+                                         int32_t n_q, int32_t n_heads,
+                                         int32_t n_kv_heads, int32_t head_dim);
+
+/* As pkv_attn_paged_verify with total_k = seq_lens[r] + n_q over slot
+ * slots[r].  Bit-identical to the paged call on the same rows. */
+int32_t pkv_attn_contig_verify(const pkv_contig *cache, const int32_t *slots,
+                               const int32_t *seq_lens, int32_t M, int32_t n_q,
+                               int32_t layer, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim,
+                               const float *Q_dev, float scale, float *out_dev,
+                               void *ws_dev, size_t ws_bytes, void *stream);
+
 /* As pkv_attn_paged_prefill with total_k = seq_lens[r] + n_q over slot
  * slots[r].  Bit-identical to the paged call on the same rows. */
 int32_t pkv_attn_contig_prefill(const pkv_contig *cache, const int32_t *slots,
@@ -352,7 +391,8 @@ int32_t pkv_pool_free_stack(pkv_pool *pool, int64_t *out, int32_t cap);
 #define PKV_K_MERGE 2    /* the merge of the decode key splits */
 #define PKV_K_PREFILL 3
 #define PKV_K_COW 4
-#define PKV_K_COUNT 5
+#define PKV_K_VERIFY 5   /* the split multi-query kernel */
+#define PKV_K_COUNT 6
 
 /* on != 0: record a HIP event pair on the launch stream around every kernel
  * the pool launches; on == 0: stop.  Either way, clears the totals. */

@@ -17,14 +17,14 @@ import numpy as np
 
 from . import _lib
 from ._lib import (BAD_ARG, BAD_DIM, BAD_GQA, CAPACITY, DEVICE, ERR_SEQ,
-                   K_APPEND, K_COW, K_DECODE, K_MERGE, K_PREFILL, OK, OOM,
-                   SIZE_MAX, UNSUPPORTED, Contig, PKVError)
+                   K_APPEND, K_COW, K_DECODE, K_MERGE, K_PREFILL, K_VERIFY, OK,
+                   OOM, SIZE_MAX, UNSUPPORTED, Contig, PKVError)
 
 __all__ = [
     "Pool", "ContigCache", "Rope", "PKVError", "lib", "pool_storage_bytes",
     "OK", "BAD_DIM", "BAD_GQA", "ERR_SEQ", "OOM", "CAPACITY", "BAD_ARG",
     "DEVICE", "UNSUPPORTED", "K_APPEND", "K_DECODE", "K_MERGE", "K_PREFILL",
-    "K_COW",
+    "K_COW", "K_VERIFY",
 ]
 
 
@@ -216,6 +216,22 @@ class Pool:
             self._h, _vp(a), a.size, layer, n_heads, n_kv_heads, head_dim, qp,
             float(scale), op, wp, wb, _stream(stream)), "attn_paged_decode", check)
 
+    def verify_workspace_bytes(self, seqs, n_q, n_heads):
+        a = _ids(seqs)
+        return lib().pkv_verify_workspace_bytes(self._h, _vp(a), a.size, n_q, n_heads)
+
+    def attn_paged_verify(self, seqs, n_q, layer, n_heads, n_kv_heads, head_dim,
+                          Q, scale, out, ws=None, stream=None, check=False):
+        a = _ids(seqs)
+        q_dim = n_heads * head_dim
+        qp = _dptr(Q, "Q", a.size * n_q * q_dim)
+        op = _dptr(out, "out", a.size * n_q * q_dim)
+        wp = None if ws is None else C.c_void_p(ws.data_ptr())
+        wb = 0 if ws is None else ws.numel() * ws.element_size()
+        return _check(lib().pkv_attn_paged_verify(
+            self._h, _vp(a), a.size, n_q, layer, n_heads, n_kv_heads, head_dim, qp,
+            float(scale), op, wp, wb, _stream(stream)), "attn_paged_verify", check)
+
     def attn_paged_prefill(self, seqs, n_q, layer, n_heads, n_kv_heads,
                            head_dim, Q, causal, scale, out, stream=None,
                            check=False):
@@ -307,6 +323,23 @@ class ContigCache:
             self.n_kv_heads, self.head_dim, _dptr(Q, "Q", s.size * q_dim),
             float(scale), _dptr(out, "out", s.size * q_dim), wp, wb,
             _stream(stream)), "attn_contig_decode", check)
+
+    def verify_workspace_bytes(self, seq_lens, n_q, n_heads):
+        l = _ids(seq_lens)
+        return lib().pkv_contig_verify_workspace_bytes(
+            _vp(l), l.size, n_q, n_heads, self.n_kv_heads, self.head_dim)
+
+    def attn_verify(self, slots, seq_lens, n_q, layer, n_heads, Q, scale, out,
+                    ws=None, stream=None, check=True):
+        s, l = _ids(slots), _ids(seq_lens)
+        q_dim = n_heads * self.head_dim
+        wp = None if ws is None else C.c_void_p(ws.data_ptr())
+        wb = 0 if ws is None else ws.numel() * ws.element_size()
+        return _check(lib().pkv_attn_contig_verify(
+            C.byref(self.desc), _vp(s), _vp(l), s.size, n_q, layer, n_heads,
+            self.n_kv_heads, self.head_dim, _dptr(Q, "Q", s.size * n_q * q_dim),
+            float(scale), _dptr(out, "out", s.size * n_q * q_dim), wp, wb,
+            _stream(stream)), "attn_contig_verify", check)
 
     def attn_prefill(self, slots, seq_lens, n_q, layer, n_heads, Q, causal,
                      scale, out, stream=None, check=True):

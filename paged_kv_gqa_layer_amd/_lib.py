@@ -21,7 +21,7 @@ BAD_ARG = 6
 DEVICE = 7
 UNSUPPORTED = 8
 
-K_APPEND, K_DECODE, K_MERGE, K_PREFILL, K_COW = range(5)
+K_APPEND, K_DECODE, K_MERGE, K_PREFILL, K_COW, K_VERIFY = range(6)
 
 SIZE_MAX = (1 << 64) - 1
 
@@ -60,6 +60,9 @@ SIGNATURES = {
                                      _F, _P, _P, _SZ, _P]),
     "pkv_attn_paged_prefill": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32,
                                       _I32, _P, _I32, _F, _P, _P]),
+    "pkv_verify_workspace_bytes": (_SZ, [_P, _P, _I32, _I32, _I32]),
+    "pkv_attn_paged_verify": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
+                                     _P, _F, _P, _P, _SZ, _P]),
     "pkv_contig_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "pkv_contig_append": (_I32, [_CP, _P, _P, _I32, _I32, _I32, _P, _P, _P]),
     "pkv_contig_decode_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32]),
@@ -67,6 +70,9 @@ SIGNATURES = {
                                       _P, _F, _P, _P, _SZ, _P]),
     "pkv_attn_contig_prefill": (_I32, [_CP, _P, _P, _I32, _I32, _I32, _I32,
                                        _I32, _I32, _P, _I32, _F, _P, _P]),
+    "pkv_contig_verify_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32, _I32, _I32]),
+    "pkv_attn_contig_verify": (_I32, [_CP, _P, _P, _I32, _I32, _I32, _I32, _I32,
+                                      _I32, _P, _F, _P, _P, _SZ, _P]),
     "pkv_seq_len": (_I32, [_P, _I32]),
     "pkv_seq_pages": (_I32, [_P, _I32, _P, _I32]),
     "pkv_pool_refcounts": (_I32, [_P, _P]),

@@ -209,16 +209,17 @@ struct RowPlan {
 };
 
 // Row blob: RowDesc[M] then tail_rows.  rowinfo(r) gives (start, pt_off);
-// the decode plan assumes total_k = start + 1 and kDecodeSplit keys/split.
+// the split plan is for n_q new rows per sequence (total_k = start + n_q)
+// and kDecodeSplit keys per split.
 template <class F>
-RowPlan build_rows(std::vector<int32_t>& v, int32_t M, F rowinfo) {
+RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, F rowinfo) {
   RowPlan pl;
   v.assign(static_cast<size_t>(M) * pkv::kRowInts, 0);
   std::vector<std::pair<int32_t, int32_t>> tails;  // (partial keys, row)
   int32_t slots = 0;
   for (int32_t r = 0; r < M; ++r) {
     const std::pair<int32_t, int32_t> info = rowinfo(r);
-    const int64_t total_k = static_cast<int64_t>(info.first) + 1;
+    const int64_t total_k = static_cast<int64_t>(info.first) + n_q;
     const int32_t nsp = ceil_div(total_k, pkv::kDecodeSplit);
     const int32_t rem = static_cast<int32_t>(total_k % pkv::kDecodeSplit);
     int32_t* d = v.data() + static_cast<size_t>(r) * pkv::kRowInts;
@@ -309,23 +310,24 @@ hipError_t size_mirror(pkv_pool* p, hipStream_t st) {
   return hipSuccess;
 }
 
-// Row descriptors of this batch on the device, with the pending page-table
-// patches applied to the mirror first.  Rows and patches travel in one
+// Row descriptors of this batch (n new rows per sequence) on the device,
+// with the pending page-table patches applied to the mirror first.  Rows and patches travel in one
 // upload, which is skipped when the device copy already describes this batch
 // at this pool version (no patches can be pending then: every page-table
 // change bumps the version).
-hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M,
+hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
                      hipStream_t st, const int32_t** rows_dev) {
   hipError_t e = size_mirror(p, st);
   if (e != hipSuccess) return e;
   std::vector<int64_t> key;
-  key.reserve(M + 2);
+  key.reserve(M + 3);
   key.push_back(static_cast<int64_t>(p->meta.version()));
   key.push_back(p->stride);
+  key.push_back(n);
   key.insert(key.end(), seqs, seqs + M);
   auto& pt = p->meta.patches();
   if (key != p->rows_key || !pt.empty()) {
-    p->plan = build_rows(p->rows, M, [&](int32_t r) {
+    p->plan = build_rows(p->rows, M, n, [&](int32_t r) {
       return std::make_pair(p->meta.seq(seqs[r])->seq_len,
                             static_cast<int32_t>(seqs[r] * p->stride));
     });
@@ -390,20 +392,34 @@ ContigMap make_contig_map(const pkv_contig* c, int32_t layer) {
   return cm;
 }
 
-// Decode partial results a batch needs: only the specialised kernel splits.
-size_t partial_bytes(const RowPlan& pl, int32_t n_heads, int32_t head_dim) {
+// Split partial results a batch needs (for n_q queries per row).
+size_t partial_bytes(const RowPlan& pl, int32_t n_q, int32_t n_heads,
+                     int32_t head_dim) {
   if (pl.max_splits <= 1) return 0;
-  return static_cast<size_t>(pl.n_items) * n_heads * (head_dim + 2) * sizeof(float);
+  return static_cast<size_t>(pl.n_items) * n_q * n_heads * (head_dim + 2) *
+         sizeof(float);
 }
 
-// Launch attention (decode: n_q == 1 and decode == true).  rows_dev points
-// at a row blob laid out by build_rows with plan `pl`.
+// Which attention entry point: decode (one query per row), verify (a few
+// offset-causal queries per row, split over keys), prefill (a chunk).
+enum class Kind { kDecode, kVerify, kPrefill };
+
+// Whether this call runs a split kernel (and so needs a workspace).
+bool uses_splits(Kind k, int32_t head_dim, int32_t group, int32_t block,
+                 int32_t n_q) {
+  if (k == Kind::kPrefill) return false;
+  if (n_q == 1 && pkv::fast_decode_ok(head_dim, group, block)) return true;
+  return k == Kind::kVerify && pkv::fast_verify_ok(head_dim, group, block, n_q);
+}
+
+// Launch attention.  rows_dev points at a row blob laid out by build_rows
+// with plan `pl` for n_q rows.
 template <class Map>
 int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
                       const RowPlan& pl, const float* Q, float* out, void* ws,
                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                       int32_t n_q, int32_t causal, float scale, int32_t M,
-                      int32_t block_size, bool decode, const double2* rope,
+                      int32_t block_size, Kind kind, const double2* rope,
                       hipStream_t st) {
   const int32_t group = n_heads / n_kv_heads;
   AttnArgs a;
@@ -413,7 +429,7 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   a.out = out;
   a.part_o = static_cast<float*>(ws);
   a.part_ml = ws ? static_cast<float*>(ws) +
-                       static_cast<size_t>(pl.n_items) * n_heads * head_dim
+                       static_cast<size_t>(pl.n_items) * n_q * n_heads * head_dim
                  : nullptr;
   a.n_full_items = pl.n_full;
   a.n_rows = M;
@@ -426,16 +442,19 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   a.n_items = pl.n_items;
   a.rope = rope;
   hipError_t e;
-  if (decode && pkv::fast_decode_ok(head_dim, group, block_size)) {
+  if (uses_splits(kind, head_dim, group, block_size, n_q)) {
     {
-      DeviceCtx::ProfScope ps(&dev, PKV_K_DECODE, st);
-      if ((e = pkv::launch_decode_fast(map, a, group, st)) != hipSuccess)
-        return PKV_ERR_DEVICE;
+      const bool one = n_q == 1 && pkv::fast_decode_ok(head_dim, group, block_size);
+      DeviceCtx::ProfScope ps(&dev, one ? PKV_K_DECODE : PKV_K_VERIFY, st);
+      e = one ? pkv::launch_decode_fast(map, a, group, st)
+              : pkv::launch_verify_mfma(map, a, group, st);
+      if (e != hipSuccess) return PKV_ERR_DEVICE;
     }
     if (pl.max_splits <= 1) return PKV_OK;
     DeviceCtx::ProfScope ps(&dev, PKV_K_MERGE, st);
     return dev_status(pkv::launch_merge(a, st));
   }
+  const bool decode = kind == Kind::kDecode;
   if (!decode && pkv::fast_prefill_ok(head_dim, group, block_size)) {
     DeviceCtx::ProfScope ps(&dev, PKV_K_PREFILL, st);
     return dev_status(pkv::launch_prefill_mfma(map, a, st));
@@ -644,7 +663,7 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
   const int32_t* rows = nullptr;
-  if (pool_rows(pool, seqs, M, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
+  if (pool_rows(pool, seqs, M, n_new, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
   const PagedMap pm = make_paged_map(pool, layer);
   DeviceCtx::ProfScope ps(&pool->dev, PKV_K_APPEND, st);
   return dev_status(pkv::launch_append(
@@ -658,53 +677,30 @@ int32_t pkv_advance(pkv_pool* pool, const int32_t* seqs, int32_t M, int32_t n) {
   return pool->meta.advance(seqs, M, n);
 }
 
-size_t pkv_decode_workspace_bytes(pkv_pool* pool, const int32_t* seqs,
-                                  int32_t M, int32_t n_heads) {
-  if (!pool || M <= 0 || n_heads <= 0) return static_cast<size_t>(-1);
+namespace {
+
+size_t pool_workspace_bytes(pkv_pool* pool, const int32_t* seqs, int32_t M,
+                            int32_t n_q, int32_t n_heads, Kind kind) {
+  if (!pool || M <= 0 || n_q <= 0 || n_heads <= 0) return static_cast<size_t>(-1);
   const auto& m = pool->meta;
   if (n_heads % m.n_kv_heads() != 0) return static_cast<size_t>(-1);
   if (m.check_batch(seqs, M) != PKV_OK) return static_cast<size_t>(-1);
-  if (!pkv::fast_decode_ok(m.head_dim(), n_heads / m.n_kv_heads(), m.block_size()))
+  if (!uses_splits(kind, m.head_dim(), n_heads / m.n_kv_heads(), m.block_size(), n_q))
     return 0;
   std::vector<int32_t> tmp;
-  const RowPlan pl = build_rows(tmp, M, [&](int32_t r) {
+  const RowPlan pl = build_rows(tmp, M, n_q, [&](int32_t r) {
     return std::make_pair(m.seq(seqs[r])->seq_len, 0);
   });
-  return partial_bytes(pl, n_heads, m.head_dim());
+  return partial_bytes(pl, n_q, n_heads, m.head_dim());
 }
 
-int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
-                              int32_t layer, int32_t n_heads,
-                              int32_t n_kv_heads, int32_t head_dim,
-                              const float* Q_dev, float scale, float* out_dev,
-                              void* ws_dev, size_t ws_bytes, void* stream) {
-  if (!pool) return PKV_ERR_BAD_ARG;
-  if (int32_t rc = attn_front_checks(M, 1, n_heads, n_kv_heads, head_dim)) return rc;
-  const auto& m = pool->meta;
-  if (n_kv_heads != m.n_kv_heads() || head_dim != m.head_dim()) return PKV_ERR_BAD_DIM;
-  if (int32_t rc = m.check_batch(seqs, M)) return rc;
-  if (layer < 0 || layer >= m.n_layers()) return PKV_ERR_BAD_ARG;
-  if (!pool->storage) return PKV_ERR_BAD_ARG;
-  if (int32_t rc = m.check_rows(seqs, M, 1)) return rc;
-  if (int32_t rc = pool_rope_check(pool, seqs, M, 1)) return rc;
-  if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
-  const size_t need = pkv_decode_workspace_bytes(pool, seqs, M, n_heads);
-  if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
-  const hipStream_t st = as_stream(stream);
-  if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
-  const int32_t* rows = nullptr;
-  if (pool_rows(pool, seqs, M, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
-  const PagedMap pm = make_paged_map(pool, layer);
-  return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, ws_dev,
-                       n_heads, n_kv_heads, head_dim, 1, 1, scale, M,
-                       m.block_size(), true, rope_table(pool->rope), st);
-}
-
-int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
-                               int32_t n_q, int32_t layer, int32_t n_heads,
-                               int32_t n_kv_heads, int32_t head_dim,
-                               const float* Q_dev, int32_t causal, float scale,
-                               float* out_dev, void* stream) {
+// The three paged attention entry points: checks in the pages' order, then
+// the rows upload and the launch.
+int32_t paged_attention(pkv_pool* pool, const int32_t* seqs, int32_t M,
+                        int32_t n_q, int32_t layer, int32_t n_heads,
+                        int32_t n_kv_heads, int32_t head_dim, const float* Q_dev,
+                        int32_t causal, float scale, float* out_dev, void* ws_dev,
+                        size_t ws_bytes, Kind kind, void* stream) {
   if (!pool) return PKV_ERR_BAD_ARG;
   if (int32_t rc = attn_front_checks(M, n_q, n_heads, n_kv_heads, head_dim)) return rc;
   const auto& m = pool->meta;
@@ -715,14 +711,60 @@ int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (int32_t rc = m.check_rows(seqs, M, n_q)) return rc;
   if (int32_t rc = pool_rope_check(pool, seqs, M, n_q)) return rc;
   if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
+  if (kind != Kind::kPrefill) {
+    const size_t need = pool_workspace_bytes(pool, seqs, M, n_q, n_heads, kind);
+    if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
+  }
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
   const int32_t* rows = nullptr;
-  if (pool_rows(pool, seqs, M, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
+  if (pool_rows(pool, seqs, M, n_q, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
   const PagedMap pm = make_paged_map(pool, layer);
-  return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, nullptr,
-                       n_heads, n_kv_heads, head_dim, n_q, causal ? 1 : 0, scale,
-                       M, m.block_size(), false, rope_table(pool->rope), st);
+  return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, ws_dev,
+                       n_heads, n_kv_heads, head_dim, n_q, causal, scale, M,
+                       m.block_size(), kind, rope_table(pool->rope), st);
+}
+
+}  // namespace
+
+size_t pkv_decode_workspace_bytes(pkv_pool* pool, const int32_t* seqs,
+                                  int32_t M, int32_t n_heads) {
+  return pool_workspace_bytes(pool, seqs, M, 1, n_heads, Kind::kDecode);
+}
+
+size_t pkv_verify_workspace_bytes(pkv_pool* pool, const int32_t* seqs,
+                                  int32_t M, int32_t n_q, int32_t n_heads) {
+  return pool_workspace_bytes(pool, seqs, M, n_q, n_heads, Kind::kVerify);
+}
+
+int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
+                              int32_t layer, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t head_dim,
+                              const float* Q_dev, float scale, float* out_dev,
+                              void* ws_dev, size_t ws_bytes, void* stream) {
+  return paged_attention(pool, seqs, M, 1, layer, n_heads, n_kv_heads, head_dim,
+                         Q_dev, 1, scale, out_dev, ws_dev, ws_bytes, Kind::kDecode,
+                         stream);
+}
+
+int32_t pkv_attn_paged_verify(pkv_pool* pool, const int32_t* seqs, int32_t M,
+                              int32_t n_q, int32_t layer, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t head_dim,
+                              const float* Q_dev, float scale, float* out_dev,
+                              void* ws_dev, size_t ws_bytes, void* stream) {
+  return paged_attention(pool, seqs, M, n_q, layer, n_heads, n_kv_heads, head_dim,
+                         Q_dev, 1, scale, out_dev, ws_dev, ws_bytes, Kind::kVerify,
+                         stream);
+}
+
+int32_t pkv_attn_paged_prefill(pkv_pool* pool, const int32_t* seqs, int32_t M,
+                               int32_t n_q, int32_t layer, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim,
+                               const float* Q_dev, int32_t causal, float scale,
+                               float* out_dev, void* stream) {
+  return paged_attention(pool, seqs, M, n_q, layer, n_heads, n_kv_heads, head_dim,
+                         Q_dev, causal ? 1 : 0, scale, out_dev, nullptr, 0,
+                         Kind::kPrefill, stream);
 }
 
 // ---------------------------------------------------------------- contiguous
@@ -752,7 +794,7 @@ int32_t contig_rows(const pkv_contig* c, const int32_t* slots,
     if (c->rope && static_cast<int64_t>(seq_lens[r]) + n > c->rope->max_positions)
       return PKV_ERR_CAPACITY;
   }
-  *pl = build_rows(rows, M, [&](int32_t r) {
+  *pl = build_rows(rows, M, n, [&](int32_t r) {
     return std::make_pair(seq_lens[r], slots[r]);
   });
   return PKV_OK;
@@ -785,30 +827,30 @@ int32_t pkv_contig_append(const pkv_contig* cache, const int32_t* slots,
                                        st));
 }
 
-size_t pkv_contig_decode_workspace_bytes(const int32_t* seq_lens, int32_t M,
-                                         int32_t n_heads, int32_t n_kv_heads,
-                                         int32_t head_dim) {
-  if (!seq_lens || M <= 0 || n_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
-      n_heads % n_kv_heads != 0)
+namespace {
+
+size_t contig_workspace_bytes(const int32_t* seq_lens, int32_t M, int32_t n_q,
+                              int32_t n_heads, int32_t n_kv_heads,
+                              int32_t head_dim, int32_t block_size, Kind kind) {
+  if (!seq_lens || M <= 0 || n_q <= 0 || n_heads <= 0 || n_kv_heads <= 0 ||
+      head_dim <= 0 || n_heads % n_kv_heads != 0)
     return static_cast<size_t>(-1);
-  if (!pkv::fast_decode_ok(head_dim, n_heads / n_kv_heads, 16)) return 0;
   for (int32_t r = 0; r < M; ++r)
     if (seq_lens[r] < 0) return static_cast<size_t>(-1);
+  if (!uses_splits(kind, head_dim, n_heads / n_kv_heads, block_size, n_q)) return 0;
   std::vector<int32_t> tmp;
-  const RowPlan pl = build_rows(tmp, M, [&](int32_t r) {
+  const RowPlan pl = build_rows(tmp, M, n_q, [&](int32_t r) {
     return std::make_pair(seq_lens[r], 0);
   });
-  return partial_bytes(pl, n_heads, head_dim);
+  return partial_bytes(pl, n_q, n_heads, head_dim);
 }
-
-namespace {
 
 int32_t contig_attention(const pkv_contig* cache, const int32_t* slots,
                          const int32_t* seq_lens, int32_t M, int32_t n_q,
                          int32_t layer, int32_t n_heads, int32_t n_kv_heads,
                          int32_t head_dim, const float* Q_dev, int32_t causal,
                          float scale, float* out_dev, void* ws_dev,
-                         size_t ws_bytes, bool decode, void* stream) {
+                         size_t ws_bytes, Kind kind, void* stream) {
   if (int32_t rc = attn_front_checks(M, n_q, n_heads, n_kv_heads, head_dim)) return rc;
   if (!contig_valid(cache)) return PKV_ERR_BAD_ARG;
   if (n_kv_heads != cache->n_kv_heads || head_dim != cache->head_dim) return PKV_ERR_BAD_DIM;
@@ -819,9 +861,8 @@ int32_t contig_attention(const pkv_contig* cache, const int32_t* slots,
   RowPlan pl;
   if (int32_t rc = contig_rows(cache, slots, seq_lens, M, n_q, rows, &pl)) return rc;
   const int32_t group = n_heads / n_kv_heads;
-  const bool fast = decode && pkv::fast_decode_ok(head_dim, group, cache->block_size);
-  if (fast) {
-    const size_t need = partial_bytes(pl, n_heads, head_dim);
+  if (uses_splits(kind, head_dim, group, cache->block_size, n_q)) {
+    const size_t need = partial_bytes(pl, n_q, n_heads, head_dim);
     if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
   }
   DeviceCtx& dev = contig_ctx();
@@ -832,10 +873,24 @@ int32_t contig_attention(const pkv_contig* cache, const int32_t* slots,
   const ContigMap cm = make_contig_map(cache, layer);
   return run_attention(dev, cm, d, pl, Q_dev, out_dev, ws_dev, n_heads,
                        n_kv_heads, head_dim, n_q, causal, scale, M,
-                       cache->block_size, decode, rope_table(cache->rope), st);
+                       cache->block_size, kind, rope_table(cache->rope), st);
 }
 
 }  // namespace
+
+size_t pkv_contig_decode_workspace_bytes(const int32_t* seq_lens, int32_t M,
+                                         int32_t n_heads, int32_t n_kv_heads,
+                                         int32_t head_dim) {
+  return contig_workspace_bytes(seq_lens, M, 1, n_heads, n_kv_heads, head_dim, 16,
+                                Kind::kDecode);
+}
+
+size_t pkv_contig_verify_workspace_bytes(const int32_t* seq_lens, int32_t M,
+                                         int32_t n_q, int32_t n_heads,
+                                         int32_t n_kv_heads, int32_t head_dim) {
+  return contig_workspace_bytes(seq_lens, M, n_q, n_heads, n_kv_heads, head_dim, 16,
+                                Kind::kVerify);
+}
 
 int32_t pkv_attn_contig_decode(const pkv_contig* cache, const int32_t* slots,
                                const int32_t* seq_lens, int32_t M,
@@ -845,7 +900,18 @@ int32_t pkv_attn_contig_decode(const pkv_contig* cache, const int32_t* slots,
                                void* ws_dev, size_t ws_bytes, void* stream) {
   return contig_attention(cache, slots, seq_lens, M, 1, layer, n_heads,
                           n_kv_heads, head_dim, Q_dev, 1, scale, out_dev,
-                          ws_dev, ws_bytes, true, stream);
+                          ws_dev, ws_bytes, Kind::kDecode, stream);
+}
+
+int32_t pkv_attn_contig_verify(const pkv_contig* cache, const int32_t* slots,
+                               const int32_t* seq_lens, int32_t M, int32_t n_q,
+                               int32_t layer, int32_t n_heads,
+                               int32_t n_kv_heads, int32_t head_dim,
+                               const float* Q_dev, float scale, float* out_dev,
+                               void* ws_dev, size_t ws_bytes, void* stream) {
+  return contig_attention(cache, slots, seq_lens, M, n_q, layer, n_heads,
+                          n_kv_heads, head_dim, Q_dev, 1, scale, out_dev,
+                          ws_dev, ws_bytes, Kind::kVerify, stream);
 }
 
 int32_t pkv_attn_contig_prefill(const pkv_contig* cache, const int32_t* slots,
@@ -856,7 +922,7 @@ int32_t pkv_attn_contig_prefill(const pkv_contig* cache, const int32_t* slots,
                                 float scale, float* out_dev, void* stream) {
   return contig_attention(cache, slots, seq_lens, M, n_q, layer, n_heads,
                           n_kv_heads, head_dim, Q_dev, causal ? 1 : 0, scale,
-                          out_dev, nullptr, 0, false, stream);
+                          out_dev, nullptr, 0, Kind::kPrefill, stream);
 }
 
 // ------------------------------------------------------------- introspection

@@ -78,15 +78,22 @@ inline bool fast_decode_ok(int32_t head_dim, int32_t group, int32_t block) {
 inline bool fast_prefill_ok(int32_t head_dim, int32_t group, int32_t block) {
   return head_dim == 128 && block == 16 && group == 4;
 }
+// Query rows (n_q x group) the split multi-query kernel holds per kv head.
+constexpr int32_t kVerifyMaxRows = 32;
+inline bool fast_verify_ok(int32_t head_dim, int32_t group, int32_t block,
+                           int32_t n_q) {
+  return head_dim == 128 && block == 16 && n_q >= 1 &&
+         static_cast<int64_t>(n_q) * group <= kVerifyMaxRows;
+}
 
 struct AttnArgs {
   const RowDesc* rows;
   const int32_t* tail_rows;  // decode: rows of the partial-split items
   const float* Q;
   float* out;
-  float* part_o;      // [slots][n_heads][head_dim]   (decode with splits)
-  float* part_ml;     // [slots][n_heads][2]
-  int32_t n_full_items;
+  float* part_o;      // [slots][n_q][n_heads][head_dim]   (split decode)
+  float* part_ml;     // [slots][n_q][n_heads][2]
+  int32_t n_full_items;  // decode / multi-query: items before the tail items
   int32_t n_rows;
   int32_t n_heads;
   int32_t n_kv_heads;
@@ -120,7 +127,13 @@ hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
 hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
-// Merges the key splits of every row with more than one (after decode_fast).
+// Split multi-query decode (n_q x group <= kVerifyMaxRows), then launch_merge.
+hipError_t launch_verify_mfma(const PagedMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st);
+hipError_t launch_verify_mfma(const ContigMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st);
+// Merges the key splits of every row with more than one (after decode_fast
+// or verify_mfma).
 hipError_t launch_merge(const AttnArgs& a, hipStream_t st);
 hipError_t launch_generic(const PagedMap& m, const AttnArgs& a,
                           int32_t group, hipStream_t st);

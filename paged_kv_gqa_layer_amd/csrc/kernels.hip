@@ -206,32 +206,36 @@ __global__ __launch_bounds__(256) void cow_kernel(float* base,
 // Lanes own split indices for the statistics and head dims (2 each) for the
 // weighted sum, which runs over the splits in ascending order.
 // One wave merges one head j of the group.
+// Partial results of split s of a row live at slot part_base + s, laid out
+// [slot][query][head]; a decode row has one query.
 __device__ __forceinline__ void merge_head(const AttnArgs& a, int32_t row,
-                                           int32_t head, int32_t part_base,
-                                           int32_t nsp, int lane) {
+                                           int32_t qi, int32_t head,
+                                           int32_t part_base, int32_t nsp,
+                                           int lane) {
   constexpr int D = 128;
   constexpr int U = 8;  // split rows loaded together
   const int64_t H = a.n_heads;
-  const int64_t h0 = (int64_t)part_base * H + head;
+  const int64_t SH = (int64_t)a.n_q * H;  // entries per slot
+  const int64_t h0 = (int64_t)part_base * SH + (int64_t)qi * H + head;
   float mx = kNegInf;
-  for (int32_t s = lane; s < nsp; s += 64) mx = fmaxf(mx, a.part_ml[(h0 + s * H) * 2]);
+  for (int32_t s = lane; s < nsp; s += 64) mx = fmaxf(mx, a.part_ml[(h0 + s * SH) * 2]);
   mx = wave_max(mx);
   float lw = 0.f, o0 = 0.f, o1 = 0.f;
   for (int32_t s0 = 0; s0 < nsp; s0 += 64) {
     const int32_t s = s0 + lane;
     float w = 0.f;
     if (s < nsp) {
-      w = fast_exp2(a.part_ml[(h0 + s * H) * 2] - mx);
-      lw = fmaf(w, a.part_ml[(h0 + s * H) * 2 + 1], lw);
+      w = fast_exp2(a.part_ml[(h0 + s * SH) * 2] - mx);
+      lw = fmaf(w, a.part_ml[(h0 + s * SH) * 2 + 1], lw);
     }
     const int32_t cnt = min(64, nsp - s0);
-    const float* base = a.part_o + (h0 + (int64_t)s0 * H) * D + 2 * lane;
+    const float* base = a.part_o + (h0 + (int64_t)s0 * SH) * D + 2 * lane;
     int32_t t = 0;
     for (; t + U <= cnt; t += U) {
       float2 ov[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        ov[u] = *reinterpret_cast<const float2*>(base + (int64_t)(t + u) * H * D);
+        ov[u] = *reinterpret_cast<const float2*>(base + (int64_t)(t + u) * SH * D);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const float wt = __shfl(w, t + u);
@@ -241,14 +245,14 @@ __device__ __forceinline__ void merge_head(const AttnArgs& a, int32_t row,
     }
     for (; t < cnt; ++t) {
       const float wt = __shfl(w, t);
-      const float2 ov = *reinterpret_cast<const float2*>(base + (int64_t)t * H * D);
+      const float2 ov = *reinterpret_cast<const float2*>(base + (int64_t)t * SH * D);
       o0 = fmaf(wt, ov.x, o0);
       o1 = fmaf(wt, ov.y, o1);
     }
   }
   const float L = wave_sum(lw);
-  *reinterpret_cast<float2*>(a.out + ((int64_t)row * H + head) * D + 2 * lane) =
-      make_float2(o0 / L, o1 / L);
+  *reinterpret_cast<float2*>(a.out + (((int64_t)row * a.n_q + qi) * H + head) * D +
+                             2 * lane) = make_float2(o0 / L, o1 / L);
 }
 
 template <int GROUP, class Map>
@@ -491,18 +495,249 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   }
 }
 
-// Split merge kernel: one wave per (row, query head) of a row with splits,
-// four heads per workgroup.  A separate launch (rather than the last split
-// merging in place) keeps the partials coherent across XCDs through the
-// kernel boundary; an in-kernel merge needs a device-scope release per split,
-// which costs more than this launch.
+// Split merge kernel: one wave per (row, query, query head) of a row with
+// splits, four heads per workgroup.  A separate launch (rather than the last
+// split merging in place) keeps the partials coherent across XCDs through
+// the kernel boundary; an in-kernel merge needs a device-scope release per
+// split, which costs more than this launch.
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int32_t quads = (a.n_heads + 3) / 4;
-  const int32_t row = blockIdx.x / quads;
-  const int32_t head = (blockIdx.x - row * quads) * 4 + (threadIdx.x >> 6);
+  const int32_t rq = blockIdx.x / quads;  // row * n_q + query
+  const int32_t head = (blockIdx.x - rq * quads) * 4 + (threadIdx.x >> 6);
+  const int32_t row = rq / a.n_q;
+  const int32_t qi = rq - row * a.n_q;
   const RowDesc rd = a.rows[row];
   if (rd.n_splits <= 1 || head >= a.n_heads) return;
-  merge_head(a, row, head, rd.part_base, rd.n_splits, threadIdx.x & 63);
+  merge_head(a, row, qi, head, rd.part_base, rd.n_splits, threadIdx.x & 63);
+}
+
+// ---------------------------------------------------------------------------
+// Multi-query decode (a few new rows per sequence, e.g. verifying drafted
+// tokens; offset-causal), head_dim 128, 16-row pages, on FP32 MFMA 16x16x4:
+// one 64-lane wave per (work item = row x 512-key split, kv head) computes
+// all n_q x group query rows of its kv head, in RB blocks of 16 MFMA
+// columns (row rho = query * group + head in group).  Each K/V byte of the
+// split is read once from HBM, straight into MFMA operand registers.
+//
+// 16x16x4 operand/result layout: lane l supplies A[l%16][l/16] and
+// B[l/16][l%16]; accumulator r of lane l is D[4*(l/16) + r][l%16].
+// Scores are computed transposed, S^T[key][row] = K Q^T, and the output as
+// O^T[dim][row] = V^T P^T, so both leave each lane with one row's values
+// (row l%16): the softmax statistics and the rescale of O are lane-local,
+// replicated over the four lanes l%16 + 16m.  Contraction orders: step
+// s = 4t + e of S^T uses dim 16t + 4m + e in lane group m (K and Q are read
+// as float4 at 16t + 4m); step s of O^T uses key 4m + s, which is score
+// accumulator r = s of the lane; output block b gives MFMA row i the dim
+// 8i + b, so a lane's accumulators hold dims 32m + 8r + b: eight contiguous
+// floats per r.
+// ---------------------------------------------------------------------------
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float f4_at(const float4& v, int e) {
+  return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+template <int RB, class Map>
+__global__ __launch_bounds__(64) void verify_mfma_kernel(Map m, AttnArgs a,
+                                                         int32_t group) {
+  constexpr int D = 128;
+  constexpr int B = 16;
+  const int32_t G = a.n_kv_heads;
+  const int32_t item_idx = blockIdx.x / G;
+  const int32_t kvh = blockIdx.x - item_idx * G;
+  int32_t row, split;
+  if (item_idx < a.n_full_items) {
+    int32_t lo = 0, hi = a.n_rows - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (a.rows[mid].first_full <= item_idx) lo = mid; else hi = mid - 1;
+    }
+    row = lo;
+    split = item_idx - a.rows[row].first_full;
+  } else {
+    row = a.tail_rows[item_idx - a.n_full_items];
+    split = a.rows[row].n_splits - 1;
+  }
+  const RowDesc rd = a.rows[row];
+  const int32_t nsp = rd.n_splits;
+  const int32_t slot = rd.part_base + split;
+  const int lane = threadIdx.x;
+  const int i16 = lane & 15;
+  const int mq = lane >> 4;
+  const int32_t n_q = a.n_q;
+  const int32_t n_rows = n_q * group;
+  const int32_t total_k = rd.start + n_q;
+  const int32_t k_begin = split * kDecodeSplit;
+  const int32_t k_end = min(total_k, k_begin + kDecodeSplit);
+  const int32_t p_begin = k_begin / B;
+  const int32_t p_end = (k_end + B - 1) / B;
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  // This lane's query row in block rb: rho = 16 rb + i16.  Rows past
+  // n_q * group hold zeros, see every key of the split and are not written.
+  int32_t q_pos[RB];
+  float4 qv[RB][8];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int32_t rho = 16 * rb + i16;
+    const bool valid = rho < n_rows;
+    const int32_t qi = valid ? rho / group : n_q - 1;
+    const int32_t hj = valid ? rho - qi * group : 0;
+    q_pos[rb] = rd.start + qi;  // total_k - n_q + qi
+    const float* qp = a.Q +
+        (((int64_t)row * n_q + qi) * a.n_heads + (int64_t)kvh * group + hj) * D + 4 * mq;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qv[rb][t] = valid ? ld4(qp + 16 * t) : zero4;
+    if (a.rope) {
+      // dims 16t + 4mq + e (t < 4) pair with the same dims + 64 (t + 4)
+      const double2* cr = a.rope + (int64_t)q_pos[rb] * (D / 2) + 4 * mq;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        rotate_pair(qv[rb][t].x, qv[rb][t + 4].x, cr[16 * t + 0]);
+        rotate_pair(qv[rb][t].y, qv[rb][t + 4].y, cr[16 * t + 1]);
+        rotate_pair(qv[rb][t].z, qv[rb][t + 4].z, cr[16 * t + 2]);
+        rotate_pair(qv[rb][t].w, qv[rb][t + 4].w, cr[16 * t + 3]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      qv[rb][t].x *= a.qscale;
+      qv[rb][t].y *= a.qscale;
+      qv[rb][t].z *= a.qscale;
+      qv[rb][t].w *= a.qscale;
+    }
+  }
+
+  floatx4 Ot[RB][8];
+  float m_run[RB], l_run[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.f;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) Ot[rb][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Page operands: K row i16, dims 16t + 4mq (t < 8); V rows 4mq + s, dims
+  // 8 i16 .. 8 i16 + 7 (vf[2s], vf[2s + 1]).  Rows past the split's end load
+  // zeros (their scores are masked; zero V keeps 0 * V finite).
+  auto load_page = [&](int32_t p, float4(&kk)[8], float4(&vv)[8]) {
+    const float* kp = m.page(rd, p, kvh);
+    const float* vp = kp + m.v_off;
+    const int32_t n_valid = min(B, k_end - p * B);
+    if (i16 < n_valid) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) kk[t] = ld4_stream(kp + i16 * D + 16 * t + 4 * mq);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) kk[t] = zero4;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int key = 4 * mq + s;
+      if (key < n_valid) {
+        vv[2 * s] = ld4_stream(vp + key * D + 8 * i16);
+        vv[2 * s + 1] = ld4_stream(vp + key * D + 8 * i16 + 4);
+      } else {
+        vv[2 * s] = vv[2 * s + 1] = zero4;
+      }
+    }
+  };
+
+  float4 kf[8], vf[8];
+  load_page(p_begin, kf, vf);
+  for (int32_t p = p_begin; p < p_end; ++p) {
+    float4 nk[8], nv[8];
+    if (p + 1 < p_end) load_page(p + 1, nk, nv);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      floatx4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t].x, qv[rb][t].x, S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t].y, qv[rb][t].y, S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t].z, qv[rb][t].z, S, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t].w, qv[rb][t].w, S, 0, 0, 0);
+      }
+      // accumulator r: key p*16 + 4mq + r of row 16 rb + i16
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int32_t key = p * B + 4 * mq + r;
+        const bool vis = key < k_end && (!a.causal || key <= q_pos[rb]);
+        if (!vis) S[r] = kNegInf;
+        mx = fmaxf(mx, S[r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[rb], mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[rb] - m_use);
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        S[r] = fast_exp2(S[r] - m_use);
+        ps += S[r];
+      }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run[rb] = fmaf(l_run[rb], alpha, ps);
+      m_run[rb] = m_new;
+#pragma unroll
+      for (int b = 0; b < 8; ++b) Ot[rb][b] *= alpha;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const float vval = f4_at(vf[2 * s2 + (b >> 2)], b & 3);
+          Ot[rb][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vval, S[s2], Ot[rb][b], 0, 0, 0);
+        }
+      }
+    }
+    if (p + 1 < p_end) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        kf[t] = nk[t];
+        vf[t] = nv[t];
+      }
+    }
+  }
+
+  // Lane (i16, mq) holds dims 32 mq + 8 r + b of row 16 rb + i16.
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int32_t rho = 16 * rb + i16;
+    if (rho >= n_rows) continue;
+    const int32_t qi = rho / group;
+    const int32_t head = kvh * group + (rho - qi * group);
+    if (nsp == 1) {
+      float* op = a.out + (((int64_t)row * n_q + qi) * a.n_heads + head) * D + 32 * mq;
+      const float L = l_run[rb];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<float4*>(op + 8 * r) =
+            make_float4(Ot[rb][0][r] / L, Ot[rb][1][r] / L, Ot[rb][2][r] / L,
+                        Ot[rb][3][r] / L);
+        *reinterpret_cast<float4*>(op + 8 * r + 4) =
+            make_float4(Ot[rb][4][r] / L, Ot[rb][5][r] / L, Ot[rb][6][r] / L,
+                        Ot[rb][7][r] / L);
+      }
+    } else {
+      const int64_t e = ((int64_t)slot * n_q + qi) * a.n_heads + head;
+      float* po = a.part_o + e * D + 32 * mq;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        *reinterpret_cast<float4*>(po + 8 * r) =
+            make_float4(Ot[rb][0][r], Ot[rb][1][r], Ot[rb][2][r], Ot[rb][3][r]);
+        *reinterpret_cast<float4*>(po + 8 * r + 4) =
+            make_float4(Ot[rb][4][r], Ot[rb][5][r], Ot[rb][6][r], Ot[rb][7][r]);
+      }
+      if (mq == 0) {
+        a.part_ml[e * 2 + 0] = m_run[rb];
+        a.part_ml[e * 2 + 1] = l_run[rb];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -884,8 +1119,22 @@ hipError_t decode_fast_impl(const Map& m, const AttnArgs& a, int32_t group,
   return hipGetLastError();
 }
 
+template <class Map>
+hipError_t verify_impl(const Map& m, const AttnArgs& a, int32_t group,
+                       hipStream_t st) {
+  const dim3 grid(a.n_items * a.n_kv_heads);
+  const int32_t rows = a.n_q * group;
+  if (rows <= 16)
+    verify_mfma_kernel<1, Map><<<grid, 64, 0, st>>>(m, a, group);
+  else if (rows <= 32)
+    verify_mfma_kernel<2, Map><<<grid, 64, 0, st>>>(m, a, group);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t merge_impl(const AttnArgs& a, hipStream_t st) {
-  merge_kernel<<<a.n_rows * ((a.n_heads + 3) / 4), 256, 0, st>>>(a);
+  merge_kernel<<<a.n_rows * a.n_q * ((a.n_heads + 3) / 4), 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -955,6 +1204,14 @@ hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,
 hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st) {
   return decode_fast_impl(m, a, group, st);
+}
+hipError_t launch_verify_mfma(const PagedMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st) {
+  return verify_impl(m, a, group, st);
+}
+hipError_t launch_verify_mfma(const ContigMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st) {
+  return verify_impl(m, a, group, st);
 }
 hipError_t launch_merge(const AttnArgs& a, hipStream_t st) {
   return merge_impl(a, st);
