@@ -30,6 +30,8 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+VERIFY_NQ = (4, 8)       # drafted tokens verified per sequence and step
+VERIFY_ROWS_MAX = 8
 FP32_MFMA_PEAK_TFLOPS = 157.3
 METRIC = ("paged GQA decode: achieved KV HBM GB/s (% peak) + "
           "seq-tokens/s at M=256")
@@ -48,6 +50,7 @@ def parse():
     ap.add_argument("--workload", default="decode_m256",
                     choices=["decode_m256", "decode_m32"])
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the oracle sample")
@@ -137,8 +140,8 @@ def bench_decode(args, synth, pkv):
     import torch
     mk = synth.decode_m256 if args.workload == "decode_m256" else synth.decode_m32
     n_steps = args.warmup + args.steps
-    # head-room for the plain run and the rotary run after it
-    wl = mk(max_steps=2 * n_steps + 1)
+    # head-room for the plain run, the rotary run and the verify runs
+    wl = mk(max_steps=2 * n_steps + 1 + VERIFY_ROWS_MAX * (n_steps + 2) * len(VERIFY_NQ))
     H, G, D = wl.n_heads, wl.n_kv_heads, wl.head_dim
     M = wl.M
     log("workload %s: M=%d, cached rows %d..%d (sum %d), pool %d blocks (%.2f GB)"
@@ -221,6 +224,72 @@ def bench_decode(args, synth, pkv):
     log("decode + rope: %.3f ms/step, %.0f GB/s step, append %.1f us, decode %.1f us"
         % (1e3 * rr["elapsed"] / args.steps, rr["gbs"], rr["kern"]["append"]["avg_us"],
            rr["kern"]["decode"]["avg_us"]))
+    if not args.no_verify:
+        res["verify"] = [bench_verify(args, wl, pool, seqs, n_q, pkv, torch)
+                         for n_q in VERIFY_NQ]
+    return res
+
+
+def bench_verify(args, wl, pool, seqs, n_q, pkv, torch):
+    """Speculative-decode verify steps on the same pool: every sequence
+    appends n_q drafted rows and attends them in one call (offset-causal),
+    then keeps a seeded 1..n_q of them and rewinds the rest (truncate)."""
+    H, G, D, M = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.M
+    n_steps = args.warmup + args.steps
+    rng = np.random.default_rng(1000 + n_q)
+    gen = np.random.default_rng(2000 + n_q)
+    Q = torch.from_numpy(gen.standard_normal((M * n_q, H * D), dtype=np.float32)).cuda()
+    K = torch.from_numpy(gen.standard_normal((M * n_q, G * D), dtype=np.float32)).cuda()
+    V = torch.from_numpy(gen.standard_normal((M * n_q, G * D), dtype=np.float32)).cuda()
+    out = torch.empty_like(Q)
+    seqs_np = np.asarray(seqs, np.int32)
+    max_len = max(pool.seq_len(s) for s in seqs) + n_q * (n_steps + 1)
+    ws = torch.empty(M * math.ceil(max_len / 512) * n_q * H * (D + 2) * 4,
+                     dtype=torch.uint8, device="cuda")
+    accept = rng.integers(1, n_q + 1, size=(n_steps, M))
+
+    def step(t):
+        pool.ensure_append(seqs_np, n_q, check=True)
+        pool.append_layer(seqs_np, n_q, 0, K, V, check=True)
+        pool.attn_paged_verify(seqs_np, n_q, 0, H, G, D, Q, wl.scale, out, ws=ws,
+                               check=True)
+        pool.advance(seqs_np, n_q, check=True)
+        for r, s in enumerate(seqs):
+            pool.seq_truncate(s, lens[r] + int(accept[t, r]), check=True)
+            lens[r] += int(accept[t, r])
+
+    lens = [pool.seq_len(s) for s in seqs]
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    kv_bytes = 0
+    for t in range(args.warmup, n_steps):
+        kv_bytes += (sum(lens) + int(accept[args.warmup:t].sum()) + M * n_q) * 2 * wl.kv_dim * 4
+    pool.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, n_steps):
+        step(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {}
+    for name, kid in (("append", pkv.K_APPEND), ("verify", pkv.K_VERIFY),
+                      ("merge", pkv.K_MERGE), ("cow", pkv.K_COW)):
+        ms, n = pool.profile_read(kid)
+        kern[name] = (1e3 * ms / n) if n else 0.0
+    pool.profile_enable(False)
+    ver_s = kern["verify"] * 1e-6 * args.steps
+    res = {
+        "n_q": n_q, "ms_per_step": 1e3 * elapsed / args.steps,
+        "gbs": kv_bytes / elapsed / 1e9, "kernel_gbs": kv_bytes / ver_s / 1e9,
+        "kernels_us": kern,
+        "accepted_tokens_per_s": float(accept[args.warmup:].sum()) / elapsed,
+        "step": "ensure_append(n_q) + append_layer + attn_paged_verify + advance "
+                "+ truncate to 1..n_q accepted",
+    }
+    log("verify n_q=%d: %.3f ms/step, %.0f GB/s step, kernel %.1f us -> %.0f GB/s, merge %.1f us"
+        % (n_q, res["ms_per_step"], res["gbs"], kern["verify"], res["kernel_gbs"],
+           kern["merge"]))
     return res
 
 
@@ -361,6 +430,7 @@ def main():
         "kv_bytes_per_step": d["kv_bytes"] / args.steps,
         "kernels_us": {k: v["avg_us"] for k, v in d["kern"].items()},
         "rope": d["rope"],
+        "verify": d.get("verify"),
         "roofline": {
             "bound": "hbm", "achieved": d["achieved"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": d["achieved"] / HBM_PEAK_GBS,

@@ -261,8 +261,8 @@ size_t pkv_verify_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
  * source": header, "truncate unref" as the speculative-decode rewind; the
  * result is the prefill's, "nx_f32_attn_paged.nx source" header comment).
  * Q_dev, out_dev: [M * n_q, n_heads * head_dim], row r * n_q + i.  Keys are
- * cut into the decode's fixed 512-row splits, merged in a fixed order, so
- * each output depends only on its own sequence.  Split kernel when
+ * cut into fixed splits (512 rows for n_q <= 4, 1024 above), merged in a
+ * fixed order, so each output depends only on its own sequence.  Split kernel when
  * n_q * (n_heads / n_kv_heads) <= 32 with head_dim 128 and 16-row pages
  * (n_q == 1 runs pkv_attn_paged_decode's kernels, bit for bit); other shapes
  * run the prefill kernels and need no workspace.  ws_dev: >=

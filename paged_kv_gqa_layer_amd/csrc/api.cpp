@@ -210,18 +210,19 @@ struct RowPlan {
 
 // Row blob: RowDesc[M] then tail_rows.  rowinfo(r) gives (start, pt_off);
 // the split plan is for n_q new rows per sequence (total_k = start + n_q)
-// and kDecodeSplit keys per split.
+// and split_keys(n_q) keys per split.
 template <class F>
 RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, F rowinfo) {
   RowPlan pl;
+  const int32_t split = pkv::split_keys(n_q);
   v.assign(static_cast<size_t>(M) * pkv::kRowInts, 0);
   std::vector<std::pair<int32_t, int32_t>> tails;  // (partial keys, row)
   int32_t slots = 0;
   for (int32_t r = 0; r < M; ++r) {
     const std::pair<int32_t, int32_t> info = rowinfo(r);
     const int64_t total_k = static_cast<int64_t>(info.first) + n_q;
-    const int32_t nsp = ceil_div(total_k, pkv::kDecodeSplit);
-    const int32_t rem = static_cast<int32_t>(total_k % pkv::kDecodeSplit);
+    const int32_t nsp = ceil_div(total_k, split);
+    const int32_t rem = static_cast<int32_t>(total_k % split);
     int32_t* d = v.data() + static_cast<size_t>(r) * pkv::kRowInts;
     d[0] = info.first;
     d[1] = info.second;
@@ -441,6 +442,7 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   a.qscale = static_cast<float>(static_cast<double>(scale) * kLog2e);
   a.n_items = pl.n_items;
   a.rope = rope;
+  a.split_keys = pkv::split_keys(n_q);
   hipError_t e;
   if (uses_splits(kind, head_dim, group, block_size, n_q)) {
     {

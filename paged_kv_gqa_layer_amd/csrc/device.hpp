@@ -7,7 +7,8 @@
 // batch row (uploaded once per pool version and batch, so all layers of a
 // step share it).
 //
-// Decode work items: each row's keys are cut into 512-key splits.  Items
+// Decode work items: each row's keys are cut into fixed splits (512 keys for
+// up to four new rows per sequence, 1024 beyond).  Items
 // 0 .. n_full_items-1 are the full splits, numbered row by row (the kernel
 // finds an item's row by binary search over first_full); the remaining
 // items are the rows' partial last splits, longest first (tail_rows), so the
@@ -67,6 +68,10 @@ struct ContigMap {
 // Key positions per split of the specialised decode kernel (a multiple of
 // its 16-row page).
 constexpr int32_t kDecodeSplit = 512;
+// Key positions per split for n_q new rows per sequence: with more query
+// rows per kv head each key costs more work, so splits are longer and the
+// partial results fewer.
+inline int32_t split_keys(int32_t n_q) { return n_q <= 4 ? kDecodeSplit : 2 * kDecodeSplit; }
 // Queries per workgroup of the MFMA prefill kernel.
 constexpr int32_t kPrefillQTile = 32;
 
@@ -105,6 +110,7 @@ struct AttnArgs {
   // rotary table [positions][head_dim/2] of (cos, sin), or null: queries are
   // turned at their positions before the scores
   const double2* rope;
+  int32_t split_keys;  // key positions per split (split_keys(n_q))
 };
 
 // Launchers (kernels.hip).  Each returns hipSuccess or the launch error.

@@ -513,23 +513,30 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Multi-query decode (a few new rows per sequence, e.g. verifying drafted
-// tokens; offset-causal), head_dim 128, 16-row pages, on FP32 MFMA 16x16x4:
-// one 64-lane wave per (work item = row x 512-key split, kv head) computes
-// all n_q x group query rows of its kv head, in RB blocks of 16 MFMA
-// columns (row rho = query * group + head in group).  Each K/V byte of the
-// split is read once from HBM, straight into MFMA operand registers.
+// tokens; offset-causal), head_dim 128, 16-row pages, on FP32 MFMA 16x16x4.
+// One workgroup per (work item = row x key split, kv head) computes all
+// n_q x group query rows of its kv head (row rho = query * group + head in
+// group), one 64-lane wave per block of 16 rows (NB = 1 or 2 waves).
 //
 // 16x16x4 operand/result layout: lane l supplies A[l%16][l/16] and
 // B[l/16][l%16]; accumulator r of lane l is D[4*(l/16) + r][l%16].
 // Scores are computed transposed, S^T[key][row] = K Q^T, and the output as
 // O^T[dim][row] = V^T P^T, so both leave each lane with one row's values
 // (row l%16): the softmax statistics and the rescale of O are lane-local,
-// replicated over the four lanes l%16 + 16m.  Contraction orders: step
-// s = 4t + e of S^T uses dim 16t + 4m + e in lane group m (K and Q are read
-// as float4 at 16t + 4m); step s of O^T uses key 4m + s, which is score
-// accumulator r = s of the lane; output block b gives MFMA row i the dim
-// 8i + b, so a lane's accumulators hold dims 32m + 8r + b: eight contiguous
-// floats per r.
+// replicated over the four lanes l%16 + 16m.
+//
+// Pages are read in row layout -- lane (m, c) = (l/16, l%16) loads positions
+// 4i + m, dims [4c, 4c+4) and [64+4c, 64+4c+4): four 256-byte runs per
+// load -- which is directly the A operand of O^T: PV step s contracts over
+// key 4s + m, and output block b = 4 half + e gives MFMA row c the dim
+// 64 half + 4c + e.  The K operand needs one key per lane, so K goes through
+// LDS: lane (c, m) reads key sigma(c) = 4 (c % 4) + c / 4 at dims 16t + 4m
+// (score step 4t + e contracts over dim 16t + 4m + e, the same order as the
+// Q operand), which makes score accumulator r of lane group m the score of
+// key 4r + m -- the key PV step r needs from that lane.
+// One wave keeps V in registers and only K in LDS (no barrier: a wave's LDS
+// accesses are in order).  Two waves split each page's loads and share K and
+// V through double-buffered LDS tiles, one barrier per page.
 // ---------------------------------------------------------------------------
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -537,11 +544,16 @@ __device__ __forceinline__ float f4_at(const float4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
-template <int RB, class Map>
-__global__ __launch_bounds__(64) void verify_mfma_kernel(Map m, AttnArgs a,
-                                                         int32_t group) {
+template <int NB, class Map>
+__global__ __launch_bounds__(64 * NB) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
   constexpr int D = 128;
   constexpr int B = 16;
+  constexpr int KS = 132;  // padded LDS row strides of the K / V tiles
+  constexpr int VS = 136;
+  constexpr int NBUF = NB == 1 ? 1 : 2;
+  __shared__ float Ks_all[NBUF][B * KS];
+  __shared__ float Vs_all[NBUF][NB == 1 ? 4 : B * VS];
   const int32_t G = a.n_kv_heads;
   const int32_t item_idx = blockIdx.x / G;
   const int32_t kvh = blockIdx.x - item_idx * G;
@@ -561,181 +573,214 @@ __global__ __launch_bounds__(64) void verify_mfma_kernel(Map m, AttnArgs a,
   const RowDesc rd = a.rows[row];
   const int32_t nsp = rd.n_splits;
   const int32_t slot = rd.part_base + split;
-  const int lane = threadIdx.x;
-  const int i16 = lane & 15;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int c16 = lane & 15;
   const int mq = lane >> 4;
   const int32_t n_q = a.n_q;
   const int32_t n_rows = n_q * group;
   const int32_t total_k = rd.start + n_q;
-  const int32_t k_begin = split * kDecodeSplit;
-  const int32_t k_end = min(total_k, k_begin + kDecodeSplit);
+  const int32_t k_begin = split * a.split_keys;
+  const int32_t k_end = min(total_k, k_begin + a.split_keys);
   const int32_t p_begin = k_begin / B;
   const int32_t p_end = (k_end + B - 1) / B;
   const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  // This lane's query row in block rb: rho = 16 rb + i16.  Rows past
-  // n_q * group hold zeros, see every key of the split and are not written.
-  int32_t q_pos[RB];
-  float4 qv[RB][8];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int32_t rho = 16 * rb + i16;
-    const bool valid = rho < n_rows;
-    const int32_t qi = valid ? rho / group : n_q - 1;
-    const int32_t hj = valid ? rho - qi * group : 0;
-    q_pos[rb] = rd.start + qi;  // total_k - n_q + qi
+  // This lane's query row; rows past n_q * group hold zeros, see every key
+  // of the split and are not written.
+  const int32_t rho = 16 * wave + c16;
+  const bool valid = rho < n_rows;
+  const int32_t qi = valid ? rho / group : n_q - 1;
+  const int32_t hj = valid ? rho - qi * group : 0;
+  const int32_t q_pos = rd.start + qi;  // total_k - n_q + qi
+  float4 qv[8];  // dims 16t + 4mq .. +3
+  {
     const float* qp = a.Q +
         (((int64_t)row * n_q + qi) * a.n_heads + (int64_t)kvh * group + hj) * D + 4 * mq;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) qv[rb][t] = valid ? ld4(qp + 16 * t) : zero4;
+    for (int t = 0; t < 8; ++t) qv[t] = valid ? ld4(qp + 16 * t) : zero4;
     if (a.rope) {
       // dims 16t + 4mq + e (t < 4) pair with the same dims + 64 (t + 4)
-      const double2* cr = a.rope + (int64_t)q_pos[rb] * (D / 2) + 4 * mq;
+      const double2* cr = a.rope + (int64_t)q_pos * (D / 2) + 4 * mq;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        rotate_pair(qv[rb][t].x, qv[rb][t + 4].x, cr[16 * t + 0]);
-        rotate_pair(qv[rb][t].y, qv[rb][t + 4].y, cr[16 * t + 1]);
-        rotate_pair(qv[rb][t].z, qv[rb][t + 4].z, cr[16 * t + 2]);
-        rotate_pair(qv[rb][t].w, qv[rb][t + 4].w, cr[16 * t + 3]);
+        rotate_pair(qv[t].x, qv[t + 4].x, cr[16 * t + 0]);
+        rotate_pair(qv[t].y, qv[t + 4].y, cr[16 * t + 1]);
+        rotate_pair(qv[t].z, qv[t + 4].z, cr[16 * t + 2]);
+        rotate_pair(qv[t].w, qv[t + 4].w, cr[16 * t + 3]);
       }
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      qv[rb][t].x *= a.qscale;
-      qv[rb][t].y *= a.qscale;
-      qv[rb][t].z *= a.qscale;
-      qv[rb][t].w *= a.qscale;
+      qv[t].x *= a.qscale;
+      qv[t].y *= a.qscale;
+      qv[t].z *= a.qscale;
+      qv[t].w *= a.qscale;
     }
   }
 
-  floatx4 Ot[RB][8];
-  float m_run[RB], l_run[RB];
+  floatx4 Ot[8];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = kNegInf;
-    l_run[rb] = 0.f;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) Ot[rb][b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int b = 0; b < 8; ++b) Ot[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+  const int sig = 4 * (c16 & 3) + (c16 >> 2);
 
-  // Page operands: K row i16, dims 16t + 4mq (t < 8); V rows 4mq + s, dims
-  // 8 i16 .. 8 i16 + 7 (vf[2s], vf[2s + 1]).  Rows past the split's end load
-  // zeros (their scores are masked; zero V keeps 0 * V finite).
-  auto load_page = [&](int32_t p, float4(&kk)[8], float4(&vv)[8]) {
+  // positions 4i + mq of page p (i in [i0, i0 + NI)), row layout; rows past
+  // the split's end load zeros (masked scores; zero V keeps 0 * V finite)
+  auto load_rows = [&](int32_t p, int i0, auto& ka, auto& kb, auto& va, auto& vb) {
+    constexpr int NI = sizeof(ka) / sizeof(float4);
     const float* kp = m.page(rd, p, kvh);
     const float* vp = kp + m.v_off;
     const int32_t n_valid = min(B, k_end - p * B);
-    if (i16 < n_valid) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) kk[t] = ld4_stream(kp + i16 * D + 16 * t + 4 * mq);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) kk[t] = zero4;
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int key = 4 * mq + s;
+    for (int j = 0; j < NI; ++j) {
+      const int key = 4 * (i0 + j) + mq;
+      const int off = key * D + 4 * c16;
       if (key < n_valid) {
-        vv[2 * s] = ld4_stream(vp + key * D + 8 * i16);
-        vv[2 * s + 1] = ld4_stream(vp + key * D + 8 * i16 + 4);
+        ka[j] = ld4_stream(kp + off);
+        kb[j] = ld4_stream(kp + off + 64);
+        va[j] = ld4_stream(vp + off);
+        vb[j] = ld4_stream(vp + off + 64);
       } else {
-        vv[2 * s] = vv[2 * s + 1] = zero4;
+        ka[j] = kb[j] = va[j] = vb[j] = zero4;
       }
     }
   };
+  auto scores = [&](const float* Kt) {
+    floatx4 S = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float4 kf = *reinterpret_cast<const float4*>(&Kt[sig * KS + 16 * t + 4 * mq]);
+      S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.x, qv[t].x, S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.y, qv[t].y, S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.z, qv[t].z, S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.w, qv[t].w, S, 0, 0, 0);
+    }
+    return S;
+  };
+  // mask, online softmax, rescale of O; S becomes P (accumulator r: key
+  // p*16 + 4r + mq)
+  auto softmax_page = [&](floatx4& S, int32_t p) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int32_t key = p * B + 4 * r + mq;
+      const bool vis = key < k_end && (!a.causal || key <= q_pos);
+      if (!vis) S[r] = kNegInf;
+      mx = fmaxf(mx, S[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      S[r] = fast_exp2(S[r] - m_use);
+      ps += S[r];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l_run = fmaf(l_run, alpha, ps);
+    m_run = m_new;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) Ot[b] *= alpha;
+  };
+  // PV step s: key 4s + mq; va / vb: dims 4c + e and 64 + 4c + e
+  auto pv_step = [&](const floatx4& P, int s, const float4& va, const float4& vb) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      Ot[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(va, e), P[s], Ot[e], 0, 0, 0);
+      Ot[4 + e] = __builtin_amdgcn_mfma_f32_16x16x4f32(f4_at(vb, e), P[s], Ot[4 + e], 0, 0, 0);
+    }
+  };
 
-  float4 kf[8], vf[8];
-  load_page(p_begin, kf, vf);
-  for (int32_t p = p_begin; p < p_end; ++p) {
-    float4 nk[8], nv[8];
-    if (p + 1 < p_end) load_page(p + 1, nk, nv);
+  if constexpr (NB == 1) {
+    float* Ks = Ks_all[0];
+    float4 kA[4], kB[4], vA[4], vB[4];
+    load_rows(p_begin, 0, kA, kB, vA, vB);
+    for (int32_t p = p_begin; p < p_end; ++p) {
+      float4 nkA[4], nkB[4], nvA[4], nvB[4];
+      if (p + 1 < p_end) load_rows(p + 1, 0, nkA, nkB, nvA, nvB);
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      floatx4 S = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t].x, qv[rb][t].x, S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t].y, qv[rb][t].y, S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t].z, qv[rb][t].z, S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[t].w, qv[rb][t].w, S, 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        const int key = 4 * i + mq;
+        *reinterpret_cast<float4*>(&Ks[key * KS + 4 * c16]) = kA[i];
+        *reinterpret_cast<float4*>(&Ks[key * KS + 64 + 4 * c16]) = kB[i];
       }
-      // accumulator r: key p*16 + 4mq + r of row 16 rb + i16
-      float mx = kNegInf;
+      floatx4 S = scores(Ks);
+      softmax_page(S, p);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int32_t key = p * B + 4 * mq + r;
-        const bool vis = key < k_end && (!a.causal || key <= q_pos[rb]);
-        if (!vis) S[r] = kNegInf;
-        mx = fmaxf(mx, S[r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[rb], mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run[rb] - m_use);
-      float ps = 0.f;
+      for (int s2 = 0; s2 < 4; ++s2) pv_step(S, s2, vA[s2], vB[s2]);
+      if (p + 1 < p_end) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        S[r] = fast_exp2(S[r] - m_use);
-        ps += S[r];
-      }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      l_run[rb] = fmaf(l_run[rb], alpha, ps);
-      m_run[rb] = m_new;
-#pragma unroll
-      for (int b = 0; b < 8; ++b) Ot[rb][b] *= alpha;
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-          const float vval = f4_at(vf[2 * s2 + (b >> 2)], b & 3);
-          Ot[rb][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(vval, S[s2], Ot[rb][b], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          kA[i] = nkA[i];
+          kB[i] = nkB[i];
+          vA[i] = nvA[i];
+          vB[i] = nvB[i];
         }
       }
     }
-    if (p + 1 < p_end) {
+  } else {
+    // wave w loads positions 4i + mq for i = 2w, 2w + 1
+    float4 kA[2], kB[2], vA[2], vB[2];
+    auto store_half = [&](int buf) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        kf[t] = nk[t];
-        vf[t] = nv[t];
+      for (int j = 0; j < 2; ++j) {
+        const int key = 4 * (2 * wave + j) + mq;
+        *reinterpret_cast<float4*>(&Ks_all[buf][key * KS + 4 * c16]) = kA[j];
+        *reinterpret_cast<float4*>(&Ks_all[buf][key * KS + 64 + 4 * c16]) = kB[j];
+        *reinterpret_cast<float4*>(&Vs_all[buf][key * VS + 4 * c16]) = vA[j];
+        *reinterpret_cast<float4*>(&Vs_all[buf][key * VS + 64 + 4 * c16]) = vB[j];
       }
+    };
+    load_rows(p_begin, 2 * wave, kA, kB, vA, vB);
+    store_half(0);
+    __syncthreads();
+    for (int32_t p = p_begin; p < p_end; ++p) {
+      const int buf = (p - p_begin) & 1;
+      if (p + 1 < p_end) load_rows(p + 1, 2 * wave, kA, kB, vA, vB);
+      floatx4 S = scores(Ks_all[buf]);
+      softmax_page(S, p);
+      const float* Vt = Vs_all[buf];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+        pv_step(S, s2, *reinterpret_cast<const float4*>(&Vt[(4 * s2 + mq) * VS + 4 * c16]),
+                *reinterpret_cast<const float4*>(&Vt[(4 * s2 + mq) * VS + 64 + 4 * c16]));
+      // the other buffer was last read before the previous barrier
+      if (p + 1 < p_end) store_half(buf ^ 1);
+      __syncthreads();
     }
   }
 
-  // Lane (i16, mq) holds dims 32 mq + 8 r + b of row 16 rb + i16.
+  // accumulator r of block 4 half + e: dim 64 half + 16 mq + 4r + e of row rho
+  if (!valid) return;
+  const int32_t head = kvh * group + hj;
+  if (nsp == 1) {
+    float* dst = a.out + (((int64_t)row * n_q + qi) * a.n_heads + head) * D + 16 * mq;
+    const float L = l_run;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int32_t rho = 16 * rb + i16;
-    if (rho >= n_rows) continue;
-    const int32_t qi = rho / group;
-    const int32_t head = kvh * group + (rho - qi * group);
-    if (nsp == 1) {
-      float* op = a.out + (((int64_t)row * n_q + qi) * a.n_heads + head) * D + 32 * mq;
-      const float L = l_run[rb];
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<float4*>(dst + 4 * r) =
+          make_float4(Ot[0][r] / L, Ot[1][r] / L, Ot[2][r] / L, Ot[3][r] / L);
+      *reinterpret_cast<float4*>(dst + 64 + 4 * r) =
+          make_float4(Ot[4][r] / L, Ot[5][r] / L, Ot[6][r] / L, Ot[7][r] / L);
+    }
+  } else {
+    const int64_t e = ((int64_t)slot * n_q + qi) * a.n_heads + head;
+    float* dst = a.part_o + e * D + 16 * mq;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<float4*>(op + 8 * r) =
-            make_float4(Ot[rb][0][r] / L, Ot[rb][1][r] / L, Ot[rb][2][r] / L,
-                        Ot[rb][3][r] / L);
-        *reinterpret_cast<float4*>(op + 8 * r + 4) =
-            make_float4(Ot[rb][4][r] / L, Ot[rb][5][r] / L, Ot[rb][6][r] / L,
-                        Ot[rb][7][r] / L);
-      }
-    } else {
-      const int64_t e = ((int64_t)slot * n_q + qi) * a.n_heads + head;
-      float* po = a.part_o + e * D + 32 * mq;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *reinterpret_cast<float4*>(po + 8 * r) =
-            make_float4(Ot[rb][0][r], Ot[rb][1][r], Ot[rb][2][r], Ot[rb][3][r]);
-        *reinterpret_cast<float4*>(po + 8 * r + 4) =
-            make_float4(Ot[rb][4][r], Ot[rb][5][r], Ot[rb][6][r], Ot[rb][7][r]);
-      }
-      if (mq == 0) {
-        a.part_ml[e * 2 + 0] = m_run[rb];
-        a.part_ml[e * 2 + 1] = l_run[rb];
-      }
+    for (int r = 0; r < 4; ++r) {
+      *reinterpret_cast<float4*>(dst + 4 * r) =
+          make_float4(Ot[0][r], Ot[1][r], Ot[2][r], Ot[3][r]);
+      *reinterpret_cast<float4*>(dst + 64 + 4 * r) =
+          make_float4(Ot[4][r], Ot[5][r], Ot[6][r], Ot[7][r]);
+    }
+    if (mq == 0) {
+      a.part_ml[e * 2 + 0] = m_run;
+      a.part_ml[e * 2 + 1] = l_run;
     }
   }
 }
@@ -1127,7 +1172,7 @@ hipError_t verify_impl(const Map& m, const AttnArgs& a, int32_t group,
   if (rows <= 16)
     verify_mfma_kernel<1, Map><<<grid, 64, 0, st>>>(m, a, group);
   else if (rows <= 32)
-    verify_mfma_kernel<2, Map><<<grid, 64, 0, st>>>(m, a, group);
+    verify_mfma_kernel<2, Map><<<grid, 128, 0, st>>>(m, a, group);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
