@@ -51,6 +51,7 @@ def parse():
                     choices=["decode_m256", "decode_m32"])
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-verify", action="store_true")
+    ap.add_argument("--no-forked", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget for the oracle sample")
@@ -293,6 +294,84 @@ def bench_verify(args, wl, pool, seqs, n_q, pkv, torch):
     return res
 
 
+def bench_forked(args, synth, pkv, shared):
+    """The forked batch: one 2048-row prefix forked into 64 sequences (the
+    parent then freed, so every prefix block has 64 references), each
+    decoding its own token stream, with pkv_attn_paged_decode or (shared)
+    pkv_attn_paged_decode_shared.  Times the decode steps after the first
+    `warmup`; reports logical KV bytes (every fork's visible keys) and unique
+    bytes (prefix once + each fork's own rows) per second."""
+    import torch
+    wl = synth.forked_2048x64()
+    H, G, D, F = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.n_forks
+    pool = pkv.Pool(wl.n_blocks, wl.block_size, 1, G, D, max_seqs=F + 8)
+    pool.set_free_order(wl.free_order())
+    parent = pool.seq_new(wl.max_tokens)
+    pk, pv = wl.prefix_kv()
+    pool.ensure_append([parent], wl.prefix, check=True)
+    pool.append_layer([parent], wl.prefix, 0, torch.from_numpy(pk).cuda(),
+                      torch.from_numpy(pv).cuda(), check=True)
+    pool.advance([parent], wl.prefix, check=True)
+    forks = [pool.seq_fork(parent) for _ in range(F)]
+    pool.seq_free(parent, check=True)
+    seqs_np = np.asarray(forks, np.int32)
+
+    def step_inputs(t):
+        xs = [wl.fork_step(f, t) for f in range(F)]
+        return tuple(np.stack([x[i] for x in xs]) for i in range(3))
+    inputs = [tuple(torch.from_numpy(a).cuda() for a in x)
+              for x in synth.parallel_map(step_inputs, range(wl.steps))]
+    out = torch.empty((F, H * D), device="cuda")
+    # partial slots per row: at most the prefix in 128-key splits plus the
+    # row's own keys in 512-key splits (plain decode needs fewer)
+    slots = math.ceil(wl.prefix / 128) + math.ceil((wl.steps + 1) / 512) + 1
+    ws = torch.empty(F * slots * H * (D + 2) * 4, dtype=torch.uint8, device="cuda")
+
+    attn = pool.attn_paged_decode_shared if shared else pool.attn_paged_decode
+
+    def step(t):
+        q, k, v = inputs[t]
+        pool.ensure_append(seqs_np, 1, check=True)
+        pool.append_layer(seqs_np, 1, 0, k, v, check=True)
+        attn(seqs_np, 0, H, G, D, q, wl.scale, out, ws=ws, check=True)
+        pool.advance(seqs_np, 1, check=True)
+
+    w = min(args.warmup, wl.steps - 1)
+    for t in range(w):
+        step(t)
+    torch.cuda.synchronize()
+    pool.profile_enable(True)
+    t0 = time.perf_counter()
+    for t in range(w, wl.steps):
+        step(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kern = {}
+    for name, kid in (("append", pkv.K_APPEND), ("prefix", pkv.K_PREFIX),
+                      ("decode", pkv.K_DECODE), ("merge", pkv.K_MERGE),
+                      ("cow", pkv.K_COW)):
+        ms, n = pool.profile_read(kid)
+        kern[name] = (1e3 * ms / n) if n else 0.0
+    pool.profile_enable(False)
+    n = wl.steps - w
+    logical = sum(F * (wl.prefix + t + 1) for t in range(w, wl.steps)) * 2 * wl.kv_dim * 4
+    unique = sum(wl.prefix + F * (t + 1) for t in range(w, wl.steps)) * 2 * wl.kv_dim * 4
+    pool.close()
+    res = {
+        "workload": wl.name, "forks": F, "prefix": wl.prefix, "steps": n,
+        "ms_per_step": 1e3 * elapsed / n,
+        "logical_gbs": logical / elapsed / 1e9, "unique_gbs": unique / elapsed / 1e9,
+        "seq_tokens_per_s": F * n / elapsed, "kernels_us": kern,
+        "step": "ensure_append + append_layer + %s + advance"
+                % ("attn_paged_decode_shared" if shared else "attn_paged_decode"),
+    }
+    log("forked%s: %.3f ms/step, logical %.0f GB/s, unique %.0f GB/s, prefix %.1f us, "
+        "decode %.1f us, merge %.1f us"
+        % (" shared" if shared else "", res["ms_per_step"], res["logical_gbs"],
+           res["unique_gbs"], kern["prefix"], kern["decode"], kern["merge"]))
+    return res
+
+
 def cpu_baseline(args, wl, oracle):
     """Time the oracle on the first sequences of the same workload (decode
     step 0: every cached row plus the new one), within a wall budget."""
@@ -444,6 +523,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill:
         line["prefill"] = bench_prefill(args, synth, pkv)
+    if not args.no_forked:
+        line["forked"] = bench_forked(args, synth, pkv, shared=False)
+        line["forked_shared_prefix"] = bench_forked(args, synth, pkv, shared=True)
     if not args.no_cpu_baseline:
         import oracle
         line["cpu_baseline"] = cpu_baseline(args, wl, oracle)

@@ -249,6 +249,32 @@ int32_t pkv_attn_paged_decode(pkv_pool *pool, const int32_t *seqs, int32_t M,
                               const float *Q_dev, float scale, float *out_dev,
                               void *ws_dev, size_t ws_bytes, void *stream);
 
+/* Device workspace bytes pkv_attn_paged_decode_shared needs for this batch
+ * (prefix and split partial results); 0 if none, (size_t)-1 on bad
+ * arguments. */
+size_t pkv_decode_shared_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
+                                         int32_t M, int32_t n_heads);
+
+/* Batched decode that reads shared prefixes once ("nx_paged_kv_gate.nx
+ * source", fork: forked sequences hold the same blocks, by reference count,
+ * for their common rows).  Computes what pkv_attn_paged_decode computes.
+ * Rows of the batch whose page tables begin with the same full pages (at
+ * least 16 of them) form a group; the group's common prefix is attended once
+ * per kv head for all members' queries (MFMA), each row's remaining keys by
+ * the decode kernel, and the partial results are merged.  Outputs agree with
+ * pkv_attn_paged_decode within the float tolerance, not bit for bit, and a
+ * row's bits depend on the group it falls in (which other rows are in the
+ * batch).  Needs head_dim 128 and 16-row pages with a decode group of 1, 2,
+ * 4 or 8; other shapes run pkv_attn_paged_decode.  ws_dev: >=
+ * pkv_decode_shared_workspace_bytes bytes.  Errors as
+ * pkv_attn_paged_decode. */
+int32_t pkv_attn_paged_decode_shared(pkv_pool *pool, const int32_t *seqs,
+                                     int32_t M, int32_t layer, int32_t n_heads,
+                                     int32_t n_kv_heads, int32_t head_dim,
+                                     const float *Q_dev, float scale,
+                                     float *out_dev, void *ws_dev,
+                                     size_t ws_bytes, void *stream);
+
 /* Device workspace bytes pkv_attn_paged_verify needs for n_q queries per
  * sequence (split partial results); 0 if none, (size_t)-1 on bad arguments. */
 size_t pkv_verify_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
@@ -392,7 +418,8 @@ int32_t pkv_pool_free_stack(pkv_pool *pool, int64_t *out, int32_t cap);
 #define PKV_K_PREFILL 3
 #define PKV_K_COW 4
 #define PKV_K_VERIFY 5   /* the split multi-query kernel */
-#define PKV_K_COUNT 6
+#define PKV_K_PREFIX 6   /* the shared-prefix kernel */
+#define PKV_K_COUNT 7
 
 /* on != 0: record a HIP event pair on the launch stream around every kernel
  * the pool launches; on == 0: stop.  Either way, clears the totals. */

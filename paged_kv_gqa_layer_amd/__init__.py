@@ -17,14 +17,14 @@ import numpy as np
 
 from . import _lib
 from ._lib import (BAD_ARG, BAD_DIM, BAD_GQA, CAPACITY, DEVICE, ERR_SEQ,
-                   K_APPEND, K_COW, K_DECODE, K_MERGE, K_PREFILL, K_VERIFY, OK,
-                   OOM, SIZE_MAX, UNSUPPORTED, Contig, PKVError)
+                   K_APPEND, K_COW, K_DECODE, K_MERGE, K_PREFILL, K_PREFIX,
+                   K_VERIFY, OK, OOM, SIZE_MAX, UNSUPPORTED, Contig, PKVError)
 
 __all__ = [
     "Pool", "ContigCache", "Rope", "PKVError", "lib", "pool_storage_bytes",
     "OK", "BAD_DIM", "BAD_GQA", "ERR_SEQ", "OOM", "CAPACITY", "BAD_ARG",
     "DEVICE", "UNSUPPORTED", "K_APPEND", "K_DECODE", "K_MERGE", "K_PREFILL",
-    "K_COW", "K_VERIFY",
+    "K_COW", "K_VERIFY", "K_PREFIX",
 ]
 
 
@@ -215,6 +215,23 @@ class Pool:
         return _check(lib().pkv_attn_paged_decode(
             self._h, _vp(a), a.size, layer, n_heads, n_kv_heads, head_dim, qp,
             float(scale), op, wp, wb, _stream(stream)), "attn_paged_decode", check)
+
+    def decode_shared_workspace_bytes(self, seqs, n_heads):
+        a = _ids(seqs)
+        return lib().pkv_decode_shared_workspace_bytes(self._h, _vp(a), a.size, n_heads)
+
+    def attn_paged_decode_shared(self, seqs, layer, n_heads, n_kv_heads, head_dim,
+                                 Q, scale, out, ws=None, stream=None, check=False):
+        a = _ids(seqs)
+        q_dim = n_heads * head_dim
+        qp = _dptr(Q, "Q", a.size * q_dim)
+        op = _dptr(out, "out", a.size * q_dim)
+        wp = None if ws is None else C.c_void_p(ws.data_ptr())
+        wb = 0 if ws is None else ws.numel() * ws.element_size()
+        return _check(lib().pkv_attn_paged_decode_shared(
+            self._h, _vp(a), a.size, layer, n_heads, n_kv_heads, head_dim, qp,
+            float(scale), op, wp, wb, _stream(stream)), "attn_paged_decode_shared",
+            check)
 
     def verify_workspace_bytes(self, seqs, n_q, n_heads):
         a = _ids(seqs)

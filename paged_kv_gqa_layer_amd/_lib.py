@@ -21,7 +21,7 @@ BAD_ARG = 6
 DEVICE = 7
 UNSUPPORTED = 8
 
-K_APPEND, K_DECODE, K_MERGE, K_PREFILL, K_COW, K_VERIFY = range(6)
+K_APPEND, K_DECODE, K_MERGE, K_PREFILL, K_COW, K_VERIFY, K_PREFIX = range(7)
 
 SIZE_MAX = (1 << 64) - 1
 
@@ -60,6 +60,9 @@ SIGNATURES = {
                                      _F, _P, _P, _SZ, _P]),
     "pkv_attn_paged_prefill": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32,
                                       _I32, _P, _I32, _F, _P, _P]),
+    "pkv_decode_shared_workspace_bytes": (_SZ, [_P, _P, _I32, _I32]),
+    "pkv_attn_paged_decode_shared": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32,
+                                            _P, _F, _P, _P, _SZ, _P]),
     "pkv_verify_workspace_bytes": (_SZ, [_P, _P, _I32, _I32, _I32]),
     "pkv_attn_paged_verify": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32, _I32,
                                      _P, _F, _P, _P, _SZ, _P]),

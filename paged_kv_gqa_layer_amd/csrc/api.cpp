@@ -17,6 +17,8 @@
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <type_traits>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -202,36 +204,48 @@ std::mutex& contig_mutex() {
 
 // What a row blob holds beyond the RowDescs (see device.hpp).
 struct RowPlan {
-  int32_t n_items = 0;      // decode items = partial-result slots
+  int32_t n_items = 0;      // split decode items (the rows' own key splits)
   int32_t n_full = 0;       // full-split items
-  int32_t max_splits = 0;
+  int32_t n_slots = 0;      // partial-result slots (own splits + prefix splits)
+  int32_t max_parts = 0;    // most partial results of one row
   size_t tail_off = 0;      // int32 offset of tail_rows in the blob
+  // shared-prefix decode (empty otherwise): int32 offsets in the blob
+  int32_t n_pre_items = 0;
+  size_t pre_off = 0, group_off = 0, member_off = 0;
 };
 
-// Row blob: RowDesc[M] then tail_rows.  rowinfo(r) gives (start, pt_off);
-// the split plan is for n_q new rows per sequence (total_k = start + n_q)
-// and split_keys(n_q) keys per split.
+// One batch row as the plan sees it: cached rows, page-table offset, first
+// own key and prefix partial slots (both 0 unless a shared prefix is used).
+struct RowIn {
+  int32_t start = 0, pt_off = 0, k_off = 0, n_pre = 0;
+};
+
+// Row blob: RowDesc[M] then tail_rows.  The split plan is for n_q new rows
+// per sequence (total_k = start + n_q): the row's own keys [k_off, total_k)
+// are cut into split_keys(n_q)-key splits.
 template <class F>
 RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, F rowinfo) {
   RowPlan pl;
   const int32_t split = pkv::split_keys(n_q);
   v.assign(static_cast<size_t>(M) * pkv::kRowInts, 0);
   std::vector<std::pair<int32_t, int32_t>> tails;  // (partial keys, row)
-  int32_t slots = 0;
   for (int32_t r = 0; r < M; ++r) {
-    const std::pair<int32_t, int32_t> info = rowinfo(r);
-    const int64_t total_k = static_cast<int64_t>(info.first) + n_q;
-    const int32_t nsp = ceil_div(total_k, split);
-    const int32_t rem = static_cast<int32_t>(total_k % split);
+    const RowIn in = rowinfo(r);
+    const int64_t own = static_cast<int64_t>(in.start) + n_q - in.k_off;
+    const int32_t nsp = ceil_div(own, split);
+    const int32_t rem = static_cast<int32_t>(own % split);
     int32_t* d = v.data() + static_cast<size_t>(r) * pkv::kRowInts;
-    d[0] = info.first;
-    d[1] = info.second;
+    d[0] = in.start;
+    d[1] = in.pt_off;
     d[2] = pl.n_full;
     d[3] = nsp;
-    d[4] = slots;
+    d[4] = pl.n_slots + in.n_pre;
+    d[5] = in.k_off;
+    d[6] = in.n_pre;
     pl.n_full += rem ? nsp - 1 : nsp;
-    slots += nsp;
-    pl.max_splits = std::max(pl.max_splits, nsp);
+    pl.n_items += nsp;
+    pl.n_slots += in.n_pre + nsp;
+    pl.max_parts = std::max(pl.max_parts, in.n_pre + nsp);
     if (rem) tails.emplace_back(rem, r);
   }
   std::stable_sort(tails.begin(), tails.end(),
@@ -239,8 +253,89 @@ RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, F rowinfo) {
                       const std::pair<int32_t, int32_t>& y) { return x.first > y.first; });
   pl.tail_off = v.size();
   for (const auto& t : tails) v.push_back(t.second);
-  pl.n_items = slots;
   return pl;
+}
+
+// Shared prefixes of a decode batch ("nx_paged_kv_gate.nx source", fork:
+// forked sequences hold the same blocks, by reference count, for their
+// common rows).  Rows are grouped when their page tables begin with the same
+// full pages -- at least kMinSharedPages of them -- and a group's prefix is
+// the full pages all its members share.  Groups are found in batch order
+// (bucketed by the first block), so the plan depends only on the batch.
+constexpr int32_t kMinSharedPages = 16;
+
+struct SharedPlan {
+  std::vector<int32_t> k_off, n_pre;        // per row
+  std::vector<int32_t> groups, members, items;
+};
+
+void find_shared(const pkv::PoolMeta& m, const int32_t* seqs, int32_t M,
+                 int32_t group_heads, SharedPlan* sp) {
+  const int32_t B = m.block_size();
+  sp->k_off.assign(M, 0);
+  sp->n_pre.assign(M, 0);
+  sp->groups.clear();
+  sp->members.clear();
+  sp->items.clear();
+  std::unordered_map<int64_t, std::vector<int32_t>> by_first;
+  std::vector<int64_t> order;
+  for (int32_t r = 0; r < M; ++r) {
+    const pkv::SeqMeta* q = m.seq(seqs[r]);
+    if (q->seq_len / B < kMinSharedPages) continue;
+    auto it = by_first.find(q->pages[0]);
+    if (it == by_first.end()) {
+      order.push_back(q->pages[0]);
+      by_first[q->pages[0]].push_back(r);
+    } else {
+      it->second.push_back(r);
+    }
+  }
+  std::vector<int32_t> mem;
+  for (const int64_t first : order) {
+    const std::vector<int32_t>& bucket = by_first[first];
+    if (bucket.size() < 2) continue;
+    const pkv::SeqMeta* rep = m.seq(seqs[bucket[0]]);
+    int32_t P = rep->seq_len / B;
+    mem.assign(1, bucket[0]);
+    for (size_t i = 1; i < bucket.size(); ++i) {
+      const pkv::SeqMeta* q = m.seq(seqs[bucket[i]]);
+      const int32_t lim = std::min(q->seq_len / B, rep->seq_len / B);
+      int32_t l = 0;
+      while (l < lim && q->pages[l] == rep->pages[l]) ++l;
+      if (l < kMinSharedPages) continue;
+      mem.push_back(bucket[i]);
+      P = std::min(P, l);
+    }
+    if (mem.size() < 2) continue;
+    const int32_t keys = P * B;
+    const int32_t n_pre = ceil_div(keys, pkv::kPrefixSplit);
+    const int32_t g = static_cast<int32_t>(sp->groups.size() / 4);
+    sp->groups.insert(sp->groups.end(),
+                      {mem[0], static_cast<int32_t>(sp->members.size()),
+                       static_cast<int32_t>(mem.size()), keys});
+    for (const int32_t r : mem) {
+      sp->members.push_back(r);
+      sp->k_off[r] = keys;
+      sp->n_pre[r] = n_pre;
+    }
+    const int32_t n_rb = ceil_div(static_cast<int64_t>(mem.size()) * group_heads,
+                                  pkv::kPrefixRows);
+    for (int32_t s = 0; s < n_pre; ++s)
+      for (int32_t b = 0; b < n_rb; ++b) sp->items.insert(sp->items.end(), {g, s, b, 0});
+  }
+}
+
+// Append the shared-prefix tables to a row blob (16-byte aligned entries).
+void append_shared(std::vector<int32_t>& v, const SharedPlan& sp, RowPlan* pl) {
+  auto align4 = [&]() { while (v.size() % 4) v.push_back(0); };
+  align4();
+  pl->pre_off = v.size();
+  v.insert(v.end(), sp.items.begin(), sp.items.end());
+  pl->group_off = v.size();
+  v.insert(v.end(), sp.groups.begin(), sp.groups.end());
+  pl->member_off = v.size();
+  v.insert(v.end(), sp.members.begin(), sp.members.end());
+  pl->n_pre_items = static_cast<int32_t>(sp.items.size() / 4);
 }
 
 }  // namespace
@@ -273,6 +368,9 @@ struct pkv_pool {
   size_t patch_off = 0;  // patches follow the rows in the blob
   std::unordered_set<int64_t> seen;
   const pkv_rope* rope = nullptr;  // borrowed; null = no rotary embedding
+  bool last_shared = false;        // the last attention call grouped prefixes
+  int32_t shared_heads = 0;        // ... with this many query heads per kv head
+  SharedPlan shared;
 
   pkv_pool(int32_t nb, int32_t bs, int32_t nl, int32_t g, int32_t d, int32_t ms)
       : meta(nb, bs, nl, g, d, ms) {}
@@ -311,27 +409,39 @@ hipError_t size_mirror(pkv_pool* p, hipStream_t st) {
   return hipSuccess;
 }
 
-// Row descriptors of this batch (n new rows per sequence) on the device,
-// with the pending page-table patches applied to the mirror first.  Rows and patches travel in one
+// Row descriptors of this batch (n new rows per sequence; with
+// shared_heads > 0 -- the query heads per kv head -- grouped by shared
+// prefix) on the device, with the pending page-table patches applied to the
+// mirror first.  Rows and patches travel in one
 // upload, which is skipped when the device copy already describes this batch
 // at this pool version (no patches can be pending then: every page-table
 // change bumps the version).
 hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
-                     hipStream_t st, const int32_t** rows_dev) {
+                     int32_t shared_heads, hipStream_t st, const int32_t** rows_dev) {
   hipError_t e = size_mirror(p, st);
   if (e != hipSuccess) return e;
   std::vector<int64_t> key;
-  key.reserve(M + 3);
+  key.reserve(M + 4);
   key.push_back(static_cast<int64_t>(p->meta.version()));
   key.push_back(p->stride);
   key.push_back(n);
+  key.push_back(shared_heads);
   key.insert(key.end(), seqs, seqs + M);
   auto& pt = p->meta.patches();
   if (key != p->rows_key || !pt.empty()) {
+    const bool shared = shared_heads > 0;
+    if (shared) find_shared(p->meta, seqs, M, shared_heads, &p->shared);
     p->plan = build_rows(p->rows, M, n, [&](int32_t r) {
-      return std::make_pair(p->meta.seq(seqs[r])->seq_len,
-                            static_cast<int32_t>(seqs[r] * p->stride));
+      RowIn in;
+      in.start = p->meta.seq(seqs[r])->seq_len;
+      in.pt_off = static_cast<int32_t>(seqs[r] * p->stride);
+      if (shared) {
+        in.k_off = p->shared.k_off[r];
+        in.n_pre = p->shared.n_pre[r];
+      }
+      return in;
     });
+    if (shared) append_shared(p->rows, p->shared, &p->plan);
     // The patch kernel writes entries in parallel, so keep only the last
     // write of each (sequence, page) entry (a fork's share followed by a
     // copy-on-append replacement, for example).
@@ -396,14 +506,15 @@ ContigMap make_contig_map(const pkv_contig* c, int32_t layer) {
 // Split partial results a batch needs (for n_q queries per row).
 size_t partial_bytes(const RowPlan& pl, int32_t n_q, int32_t n_heads,
                      int32_t head_dim) {
-  if (pl.max_splits <= 1) return 0;
-  return static_cast<size_t>(pl.n_items) * n_q * n_heads * (head_dim + 2) *
+  if (pl.max_parts <= 1) return 0;
+  return static_cast<size_t>(pl.n_slots) * n_q * n_heads * (head_dim + 2) *
          sizeof(float);
 }
 
-// Which attention entry point: decode (one query per row), verify (a few
-// offset-causal queries per row, split over keys), prefill (a chunk).
-enum class Kind { kDecode, kVerify, kPrefill };
+// Which attention entry point: decode (one query per row), shared-prefix
+// decode, verify (a few offset-causal queries per row, split over keys),
+// prefill (a chunk).
+enum class Kind { kDecode, kDecodeShared, kVerify, kPrefill };
 
 // Whether this call runs a split kernel (and so needs a workspace).
 bool uses_splits(Kind k, int32_t head_dim, int32_t group, int32_t block,
@@ -430,7 +541,7 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   a.out = out;
   a.part_o = static_cast<float*>(ws);
   a.part_ml = ws ? static_cast<float*>(ws) +
-                       static_cast<size_t>(pl.n_items) * n_q * n_heads * head_dim
+                       static_cast<size_t>(pl.n_slots) * n_q * n_heads * head_dim
                  : nullptr;
   a.n_full_items = pl.n_full;
   a.n_rows = M;
@@ -443,8 +554,18 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   a.n_items = pl.n_items;
   a.rope = rope;
   a.split_keys = pkv::split_keys(n_q);
+  a.pre_items = rows_dev + pl.pre_off;
+  a.groups = rows_dev + pl.group_off;
+  a.members = rows_dev + pl.member_off;
+  a.n_pre_items = pl.n_pre_items;
   hipError_t e;
   if (uses_splits(kind, head_dim, group, block_size, n_q)) {
+    if (pl.n_pre_items > 0) {
+      if constexpr (std::is_same<Map, PagedMap>::value) {
+        DeviceCtx::ProfScope ps(&dev, PKV_K_PREFIX, st);
+        if (pkv::launch_prefix_mfma(map, a, group, st) != hipSuccess) return PKV_ERR_DEVICE;
+      }
+    }
     {
       const bool one = n_q == 1 && pkv::fast_decode_ok(head_dim, group, block_size);
       DeviceCtx::ProfScope ps(&dev, one ? PKV_K_DECODE : PKV_K_VERIFY, st);
@@ -452,11 +573,11 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
               : pkv::launch_verify_mfma(map, a, group, st);
       if (e != hipSuccess) return PKV_ERR_DEVICE;
     }
-    if (pl.max_splits <= 1) return PKV_OK;
+    if (pl.max_parts <= 1) return PKV_OK;
     DeviceCtx::ProfScope ps(&dev, PKV_K_MERGE, st);
     return dev_status(pkv::launch_merge(a, st));
   }
-  const bool decode = kind == Kind::kDecode;
+  const bool decode = kind == Kind::kDecode || kind == Kind::kDecodeShared;
   if (!decode && pkv::fast_prefill_ok(head_dim, group, block_size)) {
     DeviceCtx::ProfScope ps(&dev, PKV_K_PREFILL, st);
     return dev_status(pkv::launch_prefill_mfma(map, a, st));
@@ -665,7 +786,12 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
   const int32_t* rows = nullptr;
-  if (pool_rows(pool, seqs, M, n_new, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
+  // build the blob the following attention call will want (shared-prefix
+  // groups or not, as the last attention call), so both share one upload
+  const int32_t shared_heads =
+      pool->last_shared && n_new == 1 ? pool->shared_heads : 0;
+  if (pool_rows(pool, seqs, M, n_new, shared_heads, st, &rows) != hipSuccess)
+    return PKV_ERR_DEVICE;
   const PagedMap pm = make_paged_map(pool, layer);
   DeviceCtx::ProfScope ps(&pool->dev, PKV_K_APPEND, st);
   return dev_status(pkv::launch_append(
@@ -681,6 +807,16 @@ int32_t pkv_advance(pkv_pool* pool, const int32_t* seqs, int32_t M, int32_t n) {
 
 namespace {
 
+// Query heads per kv head to group shared prefixes with, or 0 (no grouping:
+// another kind of call, or a shape the split kernels do not cover).
+int32_t shared_heads_for(const pkv_pool* pool, Kind kind, int32_t n_heads) {
+  const auto& m = pool->meta;
+  const int32_t group = n_heads / m.n_kv_heads();
+  if (kind != Kind::kDecodeShared || !pkv::fast_decode_ok(m.head_dim(), group, m.block_size()))
+    return 0;
+  return group;
+}
+
 size_t pool_workspace_bytes(pkv_pool* pool, const int32_t* seqs, int32_t M,
                             int32_t n_q, int32_t n_heads, Kind kind) {
   if (!pool || M <= 0 || n_q <= 0 || n_heads <= 0) return static_cast<size_t>(-1);
@@ -689,9 +825,18 @@ size_t pool_workspace_bytes(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (m.check_batch(seqs, M) != PKV_OK) return static_cast<size_t>(-1);
   if (!uses_splits(kind, m.head_dim(), n_heads / m.n_kv_heads(), m.block_size(), n_q))
     return 0;
+  const int32_t sh = shared_heads_for(pool, kind, n_heads);
+  SharedPlan sp;
+  if (sh > 0) find_shared(m, seqs, M, sh, &sp);
   std::vector<int32_t> tmp;
   const RowPlan pl = build_rows(tmp, M, n_q, [&](int32_t r) {
-    return std::make_pair(m.seq(seqs[r])->seq_len, 0);
+    RowIn in;
+    in.start = m.seq(seqs[r])->seq_len;
+    if (sh > 0) {
+      in.k_off = sp.k_off[r];
+      in.n_pre = sp.n_pre[r];
+    }
+    return in;
   });
   return partial_bytes(pl, n_q, n_heads, m.head_dim());
 }
@@ -719,8 +864,13 @@ int32_t paged_attention(pkv_pool* pool, const int32_t* seqs, int32_t M,
   }
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
+  const int32_t sh = shared_heads_for(pool, kind, n_heads);
+  if (kind == Kind::kDecode || kind == Kind::kDecodeShared) {
+    pool->last_shared = sh > 0;
+    pool->shared_heads = sh;
+  }
   const int32_t* rows = nullptr;
-  if (pool_rows(pool, seqs, M, n_q, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
+  if (pool_rows(pool, seqs, M, n_q, sh, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
   const PagedMap pm = make_paged_map(pool, layer);
   return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, ws_dev,
                        n_heads, n_kv_heads, head_dim, n_q, causal, scale, M,
@@ -737,6 +887,21 @@ size_t pkv_decode_workspace_bytes(pkv_pool* pool, const int32_t* seqs,
 size_t pkv_verify_workspace_bytes(pkv_pool* pool, const int32_t* seqs,
                                   int32_t M, int32_t n_q, int32_t n_heads) {
   return pool_workspace_bytes(pool, seqs, M, n_q, n_heads, Kind::kVerify);
+}
+
+size_t pkv_decode_shared_workspace_bytes(pkv_pool* pool, const int32_t* seqs,
+                                         int32_t M, int32_t n_heads) {
+  return pool_workspace_bytes(pool, seqs, M, 1, n_heads, Kind::kDecodeShared);
+}
+
+int32_t pkv_attn_paged_decode_shared(pkv_pool* pool, const int32_t* seqs, int32_t M,
+                                     int32_t layer, int32_t n_heads,
+                                     int32_t n_kv_heads, int32_t head_dim,
+                                     const float* Q_dev, float scale, float* out_dev,
+                                     void* ws_dev, size_t ws_bytes, void* stream) {
+  return paged_attention(pool, seqs, M, 1, layer, n_heads, n_kv_heads, head_dim,
+                         Q_dev, 1, scale, out_dev, ws_dev, ws_bytes,
+                         Kind::kDecodeShared, stream);
 }
 
 int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
@@ -797,7 +962,10 @@ int32_t contig_rows(const pkv_contig* c, const int32_t* slots,
       return PKV_ERR_CAPACITY;
   }
   *pl = build_rows(rows, M, n, [&](int32_t r) {
-    return std::make_pair(seq_lens[r], slots[r]);
+    RowIn in;
+    in.start = seq_lens[r];
+    in.pt_off = slots[r];
+    return in;
   });
   return PKV_OK;
 }
@@ -842,7 +1010,9 @@ size_t contig_workspace_bytes(const int32_t* seq_lens, int32_t M, int32_t n_q,
   if (!uses_splits(kind, head_dim, n_heads / n_kv_heads, block_size, n_q)) return 0;
   std::vector<int32_t> tmp;
   const RowPlan pl = build_rows(tmp, M, n_q, [&](int32_t r) {
-    return std::make_pair(seq_lens[r], 0);
+    RowIn in;
+    in.start = seq_lens[r];
+    return in;
   });
   return partial_bytes(pl, n_q, n_heads, head_dim);
 }

@@ -26,9 +26,12 @@ struct RowDesc {
   int32_t pt_off;      // paged: offset of the row's page table in the mirror;
                        // contiguous: the cache slot
   int32_t first_full;  // decode: first full-split item of this row
-  int32_t n_splits;    // decode: splits of this row (n_q = 1), last may be partial
-  int32_t part_base;   // decode: partial-result slot of split 0
-  int32_t pad[3];
+  int32_t n_splits;    // decode: splits of the row's own keys, last may be partial
+  int32_t part_base;   // decode: partial-result slot of own split 0
+  int32_t k_off;       // first own key: keys below it form a prefix shared with
+                       // other rows of the batch (shared-prefix decode), else 0
+  int32_t n_pre;       // partial slots of the shared prefix, part_base - n_pre ..
+  int32_t pad;
 };
 constexpr int kRowInts = sizeof(RowDesc) / sizeof(int32_t);
 
@@ -111,7 +114,17 @@ struct AttnArgs {
   // turned at their positions before the scores
   const double2* rope;
   int32_t split_keys;  // key positions per split (split_keys(n_q))
+  // shared-prefix decode: prefix work items (group, split, row block) and the
+  // groups they refer to
+  const int32_t* pre_items;  // [n_pre_items][4]
+  const int32_t* groups;     // [n_groups][4]: rep row, member offset, members, prefix keys
+  const int32_t* members;    // batch rows of each group, consecutive
+  int32_t n_pre_items;
 };
+// Keys per split of the shared-prefix kernel (eight pages).
+constexpr int32_t kPrefixSplit = 128;
+// Query rows per workgroup of the shared-prefix kernel (four waves of 16).
+constexpr int32_t kPrefixRows = 64;
 
 // Launchers (kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_patch(int32_t* mirror, const int32_t* patches, int32_t n,
@@ -137,6 +150,10 @@ hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
 hipError_t launch_verify_mfma(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
 hipError_t launch_verify_mfma(const ContigMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st);
+// Shared-prefix decode: every group's prefix keys once per kv head for all
+// its members' queries, into the members' prefix partial slots.
+hipError_t launch_prefix_mfma(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
 // Merges the key splits of every row with more than one (after decode_fast
 // or verify_mfma).

@@ -278,14 +278,14 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
     split = a.rows[row].n_splits - 1;
   }
   const RowDesc rd = a.rows[row];
-  const int32_t nsp = rd.n_splits;
+  const int32_t nsp = rd.n_pre + rd.n_splits;  // partial results of the row
   const int32_t slot = rd.part_base + split;
   const int lane = threadIdx.x;
   const int rr = lane >> 4;
   const int c = lane & 15;
 
   const int32_t total_k = rd.start + 1;
-  const int32_t k_begin = split * kDecodeSplit;
+  const int32_t k_begin = rd.k_off + split * kDecodeSplit;
   const int32_t k_end = min(total_k, k_begin + kDecodeSplit);
   const int32_t p_begin = k_begin / B;
   const int32_t p_end = (k_end + B - 1) / B;
@@ -507,23 +507,23 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int32_t row = rq / a.n_q;
   const int32_t qi = rq - row * a.n_q;
   const RowDesc rd = a.rows[row];
-  if (rd.n_splits <= 1 || head >= a.n_heads) return;
-  merge_head(a, row, qi, head, rd.part_base, rd.n_splits, threadIdx.x & 63);
+  const int32_t nsp = rd.n_pre + rd.n_splits;
+  if (nsp <= 1 || head >= a.n_heads) return;
+  merge_head(a, row, qi, head, rd.part_base - rd.n_pre, nsp, threadIdx.x & 63);
 }
 
 // ---------------------------------------------------------------------------
-// Multi-query decode (a few new rows per sequence, e.g. verifying drafted
-// tokens; offset-causal), head_dim 128, 16-row pages, on FP32 MFMA 16x16x4.
-// One workgroup per (work item = row x key split, kv head) computes all
-// n_q x group query rows of its kv head (row rho = query * group + head in
-// group), one 64-lane wave per block of 16 rows (NB = 1 or 2 waves).
+// Multi-row MFMA attention engine (FP32 MFMA 16x16x4, head_dim 128, 16-row
+// pages), used by the multi-query decode and the shared-prefix kernels.  A
+// workgroup of NB waves runs 16 NB query rows of one kv head over one key
+// range; each wave owns 16 rows (lane l: row l%16).
 //
 // 16x16x4 operand/result layout: lane l supplies A[l%16][l/16] and
 // B[l/16][l%16]; accumulator r of lane l is D[4*(l/16) + r][l%16].
 // Scores are computed transposed, S^T[key][row] = K Q^T, and the output as
-// O^T[dim][row] = V^T P^T, so both leave each lane with one row's values
-// (row l%16): the softmax statistics and the rescale of O are lane-local,
-// replicated over the four lanes l%16 + 16m.
+// O^T[dim][row] = V^T P^T, so both leave each lane with one row's values:
+// the softmax statistics and the rescale of O are lane-local, replicated
+// over the four lanes l%16 + 16m.
 //
 // Pages are read in row layout -- lane (m, c) = (l/16, l%16) loads positions
 // 4i + m, dims [4c, 4c+4) and [64+4c, 64+4c+4): four 256-byte runs per
@@ -531,12 +531,12 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 // key 4s + m, and output block b = 4 half + e gives MFMA row c the dim
 // 64 half + 4c + e.  The K operand needs one key per lane, so K goes through
 // LDS: lane (c, m) reads key sigma(c) = 4 (c % 4) + c / 4 at dims 16t + 4m
-// (score step 4t + e contracts over dim 16t + 4m + e, the same order as the
-// Q operand), which makes score accumulator r of lane group m the score of
-// key 4r + m -- the key PV step r needs from that lane.
+// (score step 4t + e contracts over dim 16t + 4m + e, the order of the Q
+// operand qv[t]), which makes score accumulator r of lane group m the score
+// of key 4r + m -- the key PV step r needs from that lane.
 // One wave keeps V in registers and only K in LDS (no barrier: a wave's LDS
-// accesses are in order).  Two waves split each page's loads and share K and
-// V through double-buffered LDS tiles, one barrier per page.
+// accesses are in order).  Several waves split each page's loads and share K
+// and V through double-buffered LDS tiles, one barrier per page.
 // ---------------------------------------------------------------------------
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -544,89 +544,69 @@ __device__ __forceinline__ float f4_at(const float4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
+constexpr int kMqKS = 132;  // padded LDS row strides of the K / V tiles
+constexpr int kMqVS = 136;
+
+template <int NB>
+struct MqLds {
+  float K[NB == 1 ? 1 : 2][16 * kMqKS];
+  float V[NB == 1 ? 1 : 2][NB == 1 ? 4 : 16 * kMqVS];
+};
+
+// Q operand of one row: qp points at the row's head vector; dims
+// 16t + 4mq .. +3 land in qv[t], turned at q_pos when a rotary table is set,
+// then scaled (base-2 score units).
+__device__ __forceinline__ void mq_load_q(const float* qp, bool valid, int mq,
+                                          const double2* rope, int32_t q_pos,
+                                          float qscale, float4 (&qv)[8]) {
+  constexpr int D = 128;
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) qv[t] = valid ? ld4(qp + 16 * t + 4 * mq) : zero4;
+  if (rope) {
+    // dims 16t + 4mq + e (t < 4) pair with the same dims + 64 (t + 4)
+    const double2* cr = rope + (int64_t)q_pos * (D / 2) + 4 * mq;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      rotate_pair(qv[t].x, qv[t + 4].x, cr[16 * t + 0]);
+      rotate_pair(qv[t].y, qv[t + 4].y, cr[16 * t + 1]);
+      rotate_pair(qv[t].z, qv[t + 4].z, cr[16 * t + 2]);
+      rotate_pair(qv[t].w, qv[t + 4].w, cr[16 * t + 3]);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    qv[t].x *= qscale;
+    qv[t].y *= qscale;
+    qv[t].z *= qscale;
+    qv[t].w *= qscale;
+  }
+}
+
+// Keys [k_begin, k_end) of the pages of rd, kv head kvh; keys above q_pos
+// are masked.  Updates this lane's row state (Ot, m_run, l_run).
 template <int NB, class Map>
-__global__ __launch_bounds__(64 * NB) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
+__device__ __forceinline__ void mq_attend(const Map& m, const RowDesc& rd,
+                                          int32_t kvh, int32_t k_begin,
+                                          int32_t k_end, int32_t q_pos,
+                                          const float4 (&qv)[8], floatx4 (&Ot)[8],
+                                          float& m_run, float& l_run,
+                                          MqLds<NB>& sh) {
   constexpr int D = 128;
   constexpr int B = 16;
-  constexpr int KS = 132;  // padded LDS row strides of the K / V tiles
-  constexpr int VS = 136;
-  constexpr int NBUF = NB == 1 ? 1 : 2;
-  __shared__ float Ks_all[NBUF][B * KS];
-  __shared__ float Vs_all[NBUF][NB == 1 ? 4 : B * VS];
-  const int32_t G = a.n_kv_heads;
-  const int32_t item_idx = blockIdx.x / G;
-  const int32_t kvh = blockIdx.x - item_idx * G;
-  int32_t row, split;
-  if (item_idx < a.n_full_items) {
-    int32_t lo = 0, hi = a.n_rows - 1;
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if (a.rows[mid].first_full <= item_idx) lo = mid; else hi = mid - 1;
-    }
-    row = lo;
-    split = item_idx - a.rows[row].first_full;
-  } else {
-    row = a.tail_rows[item_idx - a.n_full_items];
-    split = a.rows[row].n_splits - 1;
-  }
-  const RowDesc rd = a.rows[row];
-  const int32_t nsp = rd.n_splits;
-  const int32_t slot = rd.part_base + split;
+  constexpr int KS = kMqKS;
+  constexpr int VS = kMqVS;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int c16 = lane & 15;
   const int mq = lane >> 4;
-  const int32_t n_q = a.n_q;
-  const int32_t n_rows = n_q * group;
-  const int32_t total_k = rd.start + n_q;
-  const int32_t k_begin = split * a.split_keys;
-  const int32_t k_end = min(total_k, k_begin + a.split_keys);
+  const int sig = 4 * (c16 & 3) + (c16 >> 2);
   const int32_t p_begin = k_begin / B;
   const int32_t p_end = (k_end + B - 1) / B;
   const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
 
-  // This lane's query row; rows past n_q * group hold zeros, see every key
-  // of the split and are not written.
-  const int32_t rho = 16 * wave + c16;
-  const bool valid = rho < n_rows;
-  const int32_t qi = valid ? rho / group : n_q - 1;
-  const int32_t hj = valid ? rho - qi * group : 0;
-  const int32_t q_pos = rd.start + qi;  // total_k - n_q + qi
-  float4 qv[8];  // dims 16t + 4mq .. +3
-  {
-    const float* qp = a.Q +
-        (((int64_t)row * n_q + qi) * a.n_heads + (int64_t)kvh * group + hj) * D + 4 * mq;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qv[t] = valid ? ld4(qp + 16 * t) : zero4;
-    if (a.rope) {
-      // dims 16t + 4mq + e (t < 4) pair with the same dims + 64 (t + 4)
-      const double2* cr = a.rope + (int64_t)q_pos * (D / 2) + 4 * mq;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        rotate_pair(qv[t].x, qv[t + 4].x, cr[16 * t + 0]);
-        rotate_pair(qv[t].y, qv[t + 4].y, cr[16 * t + 1]);
-        rotate_pair(qv[t].z, qv[t + 4].z, cr[16 * t + 2]);
-        rotate_pair(qv[t].w, qv[t + 4].w, cr[16 * t + 3]);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      qv[t].x *= a.qscale;
-      qv[t].y *= a.qscale;
-      qv[t].z *= a.qscale;
-      qv[t].w *= a.qscale;
-    }
-  }
-
-  floatx4 Ot[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) Ot[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
-  const int sig = 4 * (c16 & 3) + (c16 >> 2);
-
-  // positions 4i + mq of page p (i in [i0, i0 + NI)), row layout; rows past
-  // the split's end load zeros (masked scores; zero V keeps 0 * V finite)
+  // positions 4i + mq of page p for i in [i0, i0 + NI), row layout; rows
+  // past k_end load zeros (masked scores; zero V keeps 0 * V finite)
   auto load_rows = [&](int32_t p, int i0, auto& ka, auto& kb, auto& va, auto& vb) {
     constexpr int NI = sizeof(ka) / sizeof(float4);
     const float* kp = m.page(rd, p, kvh);
@@ -665,8 +645,7 @@ void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int32_t key = p * B + 4 * r + mq;
-      const bool vis = key < k_end && (!a.causal || key <= q_pos);
-      if (!vis) S[r] = kNegInf;
+      if (!(key < k_end && key <= q_pos)) S[r] = kNegInf;
       mx = fmaxf(mx, S[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -697,7 +676,7 @@ void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
   };
 
   if constexpr (NB == 1) {
-    float* Ks = Ks_all[0];
+    float* Ks = sh.K[0];
     float4 kA[4], kB[4], vA[4], vB[4];
     load_rows(p_begin, 0, kA, kB, vA, vB);
     for (int32_t p = p_begin; p < p_end; ++p) {
@@ -724,64 +703,184 @@ void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
       }
     }
   } else {
-    // wave w loads positions 4i + mq for i = 2w, 2w + 1
-    float4 kA[2], kB[2], vA[2], vB[2];
-    auto store_half = [&](int buf) {
+    // wave w loads positions 4i + mq for i in [w NI, (w + 1) NI)
+    constexpr int NI = 4 / NB;
+    float4 kA[NI], kB[NI], vA[NI], vB[NI];
+    auto store_part = [&](int buf) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int key = 4 * (2 * wave + j) + mq;
-        *reinterpret_cast<float4*>(&Ks_all[buf][key * KS + 4 * c16]) = kA[j];
-        *reinterpret_cast<float4*>(&Ks_all[buf][key * KS + 64 + 4 * c16]) = kB[j];
-        *reinterpret_cast<float4*>(&Vs_all[buf][key * VS + 4 * c16]) = vA[j];
-        *reinterpret_cast<float4*>(&Vs_all[buf][key * VS + 64 + 4 * c16]) = vB[j];
+      for (int j = 0; j < NI; ++j) {
+        const int key = 4 * (NI * wave + j) + mq;
+        *reinterpret_cast<float4*>(&sh.K[buf][key * KS + 4 * c16]) = kA[j];
+        *reinterpret_cast<float4*>(&sh.K[buf][key * KS + 64 + 4 * c16]) = kB[j];
+        *reinterpret_cast<float4*>(&sh.V[buf][key * VS + 4 * c16]) = vA[j];
+        *reinterpret_cast<float4*>(&sh.V[buf][key * VS + 64 + 4 * c16]) = vB[j];
       }
     };
-    load_rows(p_begin, 2 * wave, kA, kB, vA, vB);
-    store_half(0);
+    load_rows(p_begin, NI * wave, kA, kB, vA, vB);
+    store_part(0);
     __syncthreads();
     for (int32_t p = p_begin; p < p_end; ++p) {
       const int buf = (p - p_begin) & 1;
-      if (p + 1 < p_end) load_rows(p + 1, 2 * wave, kA, kB, vA, vB);
-      floatx4 S = scores(Ks_all[buf]);
+      if (p + 1 < p_end) load_rows(p + 1, NI * wave, kA, kB, vA, vB);
+      floatx4 S = scores(sh.K[buf]);
       softmax_page(S, p);
-      const float* Vt = Vs_all[buf];
+      const float* Vt = sh.V[buf];
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2)
         pv_step(S, s2, *reinterpret_cast<const float4*>(&Vt[(4 * s2 + mq) * VS + 4 * c16]),
                 *reinterpret_cast<const float4*>(&Vt[(4 * s2 + mq) * VS + 64 + 4 * c16]));
       // the other buffer was last read before the previous barrier
-      if (p + 1 < p_end) store_half(buf ^ 1);
+      if (p + 1 < p_end) store_part(buf ^ 1);
       __syncthreads();
     }
   }
+}
 
-  // accumulator r of block 4 half + e: dim 64 half + 16 mq + 4r + e of row rho
-  if (!valid) return;
-  const int32_t head = kvh * group + hj;
-  if (nsp == 1) {
-    float* dst = a.out + (((int64_t)row * n_q + qi) * a.n_heads + head) * D + 16 * mq;
-    const float L = l_run;
+// Row result: accumulator r of block 4 half + e is dim 64 half + 16 mq +
+// 4r + e.  dst points at the row's head vector; values are divided by L.
+__device__ __forceinline__ void mq_store(float* dst, int mq,
+                                         const floatx4 (&Ot)[8], float L) {
+  dst += 16 * mq;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<float4*>(dst + 4 * r) =
-          make_float4(Ot[0][r] / L, Ot[1][r] / L, Ot[2][r] / L, Ot[3][r] / L);
-      *reinterpret_cast<float4*>(dst + 64 + 4 * r) =
-          make_float4(Ot[4][r] / L, Ot[5][r] / L, Ot[6][r] / L, Ot[7][r] / L);
+  for (int r = 0; r < 4; ++r) {
+    *reinterpret_cast<float4*>(dst + 4 * r) =
+        make_float4(Ot[0][r] / L, Ot[1][r] / L, Ot[2][r] / L, Ot[3][r] / L);
+    *reinterpret_cast<float4*>(dst + 64 + 4 * r) =
+        make_float4(Ot[4][r] / L, Ot[5][r] / L, Ot[6][r] / L, Ot[7][r] / L);
+  }
+}
+__device__ __forceinline__ void mq_store_partial(float* dst, int mq,
+                                                 const floatx4 (&Ot)[8]) {
+  dst += 16 * mq;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    *reinterpret_cast<float4*>(dst + 4 * r) =
+        make_float4(Ot[0][r], Ot[1][r], Ot[2][r], Ot[3][r]);
+    *reinterpret_cast<float4*>(dst + 64 + 4 * r) =
+        make_float4(Ot[4][r], Ot[5][r], Ot[6][r], Ot[7][r]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-query decode (a few new rows per sequence, e.g. verifying drafted
+// tokens; offset-causal): one workgroup per (work item = row x key split,
+// kv head) runs all n_q x group query rows of its kv head (row rho =
+// query * group + head in group), NB = 1 or 2 waves of 16 rows.
+// ---------------------------------------------------------------------------
+template <int NB, class Map>
+__global__ __launch_bounds__(64 * NB) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
+  constexpr int D = 128;
+  __shared__ MqLds<NB> sh;
+  const int32_t G = a.n_kv_heads;
+  const int32_t item_idx = blockIdx.x / G;
+  const int32_t kvh = blockIdx.x - item_idx * G;
+  int32_t row, split;
+  if (item_idx < a.n_full_items) {
+    int32_t lo = 0, hi = a.n_rows - 1;
+    while (lo < hi) {
+      const int32_t mid = (lo + hi + 1) >> 1;
+      if (a.rows[mid].first_full <= item_idx) lo = mid; else hi = mid - 1;
     }
+    row = lo;
+    split = item_idx - a.rows[row].first_full;
   } else {
-    const int64_t e = ((int64_t)slot * n_q + qi) * a.n_heads + head;
-    float* dst = a.part_o + e * D + 16 * mq;
+    row = a.tail_rows[item_idx - a.n_full_items];
+    split = a.rows[row].n_splits - 1;
+  }
+  const RowDesc rd = a.rows[row];
+  const int32_t nsp = rd.n_pre + rd.n_splits;
+  const int32_t slot = rd.part_base + split;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int mq = lane >> 4;
+  const int32_t n_q = a.n_q;
+  const int32_t total_k = rd.start + n_q;
+  const int32_t k_begin = rd.k_off + split * a.split_keys;
+  const int32_t k_end = min(total_k, k_begin + a.split_keys);
+
+  // This lane's query row; rows past n_q * group hold zeros, see every key
+  // of the split and are not written.
+  const int32_t rho = 16 * wave + (lane & 15);
+  const bool valid = rho < n_q * group;
+  const int32_t qi = valid ? rho / group : n_q - 1;
+  const int32_t hj = valid ? rho - qi * group : 0;
+  const int32_t q_pos = rd.start + qi;  // total_k - n_q + qi
+  const int64_t qrow = ((int64_t)row * n_q + qi) * a.n_heads + (int64_t)kvh * group + hj;
+  float4 qv[8];
+  mq_load_q(a.Q + qrow * D, valid, mq, a.rope, q_pos, a.qscale, qv);
+
+  floatx4 Ot[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      *reinterpret_cast<float4*>(dst + 4 * r) =
-          make_float4(Ot[0][r], Ot[1][r], Ot[2][r], Ot[3][r]);
-      *reinterpret_cast<float4*>(dst + 64 + 4 * r) =
-          make_float4(Ot[4][r], Ot[5][r], Ot[6][r], Ot[7][r]);
-    }
+  for (int b = 0; b < 8; ++b) Ot[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+  mq_attend<NB>(m, rd, kvh, k_begin, k_end, a.causal ? q_pos : INT32_MAX, qv, Ot,
+                m_run, l_run, sh);
+
+  if (!valid) return;
+  if (nsp == 1) {
+    mq_store(a.out + qrow * D, mq, Ot, l_run);
+  } else {
+    const int64_t e = ((int64_t)slot * n_q + qi) * a.n_heads + kvh * group + hj;
+    mq_store_partial(a.part_o + e * D, mq, Ot);
     if (mq == 0) {
       a.part_ml[e * 2 + 0] = m_run;
       a.part_ml[e * 2 + 1] = l_run;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Shared-prefix decode: the batch rows of a group share their first
+// prefix_keys keys (the same blocks, by reference count after a fork).  One
+// workgroup per (prefix item = group x kPrefixSplit keys x block of
+// kPrefixRows query rows, kv head) runs those keys once for the queries of
+// up to kPrefixRows / group members (row rho = member * group + head in
+// group) and writes each member's prefix partial result.  Every prefix key
+// precedes each member's new row, so nothing is masked.
+// ---------------------------------------------------------------------------
+template <class Map>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefix_mfma_kernel(Map m, AttnArgs a, int32_t group) {
+  constexpr int D = 128;
+  constexpr int NB = kPrefixRows / 16;
+  __shared__ MqLds<NB> sh;
+  const int32_t G = a.n_kv_heads;
+  const int32_t item_idx = blockIdx.x / G;
+  const int32_t kvh = blockIdx.x - item_idx * G;
+  const int4 it = reinterpret_cast<const int4*>(a.pre_items)[item_idx];
+  const int4 gd = reinterpret_cast<const int4*>(a.groups)[it.x];
+  const int32_t split = it.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int mq = lane >> 4;
+  const int32_t k_begin = split * kPrefixSplit;
+  const int32_t k_end = min(gd.w, k_begin + kPrefixSplit);
+
+  const int32_t rho = kPrefixRows * it.z + 16 * wave + (lane & 15);
+  const bool valid = rho < gd.z * group;
+  const int32_t mi = valid ? rho / group : 0;
+  const int32_t hj = valid ? rho - mi * group : 0;
+  const int32_t row = a.members[gd.y + mi];
+  const RowDesc rd = a.rows[row];
+  const int64_t qrow = (int64_t)row * a.n_heads + (int64_t)kvh * group + hj;
+  float4 qv[8];
+  mq_load_q(a.Q + qrow * D, valid, mq, a.rope, rd.start, a.qscale, qv);
+
+  floatx4 Ot[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) Ot[b] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+  mq_attend<NB>(m, a.rows[gd.x], kvh, k_begin, k_end, INT32_MAX, qv, Ot, m_run,
+                l_run, sh);
+
+  if (!valid) return;
+  const int64_t e = (int64_t)(rd.part_base - rd.n_pre + split) * a.n_heads +
+                    kvh * group + hj;
+  mq_store_partial(a.part_o + e * D, mq, Ot);
+  if (mq == 0) {
+    a.part_ml[e * 2 + 0] = m_run;
+    a.part_ml[e * 2 + 1] = l_run;
   }
 }
 
@@ -1178,6 +1277,15 @@ hipError_t verify_impl(const Map& m, const AttnArgs& a, int32_t group,
   return hipGetLastError();
 }
 
+template <class Map>
+hipError_t prefix_impl(const Map& m, const AttnArgs& a, int32_t group,
+                       hipStream_t st) {
+  if (a.n_pre_items <= 0) return hipSuccess;
+  prefix_mfma_kernel<Map><<<a.n_pre_items * a.n_kv_heads, kPrefixRows / 16 * 64, 0, st>>>(
+      m, a, group);
+  return hipGetLastError();
+}
+
 hipError_t merge_impl(const AttnArgs& a, hipStream_t st) {
   merge_kernel<<<a.n_rows * a.n_q * ((a.n_heads + 3) / 4), 256, 0, st>>>(a);
   return hipGetLastError();
@@ -1257,6 +1365,10 @@ hipError_t launch_verify_mfma(const PagedMap& m, const AttnArgs& a,
 hipError_t launch_verify_mfma(const ContigMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st) {
   return verify_impl(m, a, group, st);
+}
+hipError_t launch_prefix_mfma(const PagedMap& m, const AttnArgs& a,
+                              int32_t group, hipStream_t st) {
+  return prefix_impl(m, a, group, st);
 }
 hipError_t launch_merge(const AttnArgs& a, hipStream_t st) {
   return merge_impl(a, st);
