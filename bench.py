@@ -122,9 +122,11 @@ class HistoryFiller:
         self.ex.shutdown()
 
 
-def traffic_for(kernel_name, launches_bytes=None):
-    """HBM traffic per launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def traffic_for(kernel_name, algorithmic_bytes_per_launch):
+    """HBM bytes per launch implied by the committed rocprofv3 counter summary
+    (its calibrated FETCH_SIZE + WRITE_SIZE over the algorithmic bytes of the
+    profiled launches, times this run's algorithmic bytes per launch), if it
+    was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "%s_traffic.json" % kernel_name)
     if not os.path.exists(path):
         return None
@@ -134,7 +136,7 @@ def traffic_for(kernel_name, launches_bytes=None):
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if t.get("kernels_hip_sha256") != sha:
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t["traffic_over_algorithmic"] * algorithmic_bytes_per_launch
 
 
 def bench_decode(args, synth, pkv):
@@ -481,7 +483,7 @@ def main():
 
     d = bench_decode(args, synth, pkv)
     wl = d["wl"]
-    traffic = traffic_for("decode_fast_kernel")
+    traffic = traffic_for("decode_fast_kernel", d["kv_bytes"] / args.steps)
     line = {
         "metric": METRIC,
         "value": d["gbs"],
