@@ -205,10 +205,9 @@ std::mutex& contig_mutex() {
 // What a row blob holds beyond the RowDescs (see device.hpp).
 struct RowPlan {
   int32_t n_items = 0;      // split decode items (the rows' own key splits)
-  int32_t n_full = 0;       // full-split items
   int32_t n_slots = 0;      // partial-result slots (own splits + prefix splits)
   int32_t max_parts = 0;    // most partial results of one row
-  size_t tail_off = 0;      // int32 offset of tail_rows in the blob
+  size_t item_off = 0;      // int32 offset of the (row, split) item list
   // shared-prefix decode (empty otherwise): int32 offsets in the blob
   int32_t n_pre_items = 0;
   size_t pre_off = 0, group_off = 0, member_off = 0;
@@ -220,15 +219,17 @@ struct RowIn {
   int32_t start = 0, pt_off = 0, k_off = 0, n_pre = 0;
 };
 
-// Row blob: RowDesc[M] then tail_rows.  The split plan is for n_q new rows
-// per sequence (total_k = start + n_q): the row's own keys [k_off, total_k)
-// are cut into split_keys(n_q)-key splits.
+// Row blob: RowDesc[M], then the split items as (row, split) pairs -- every
+// full split row by row, then the partial last splits longest first.  The
+// split plan is for n_q new rows per sequence (total_k = start + n_q): the
+// row's own keys [k_off, total_k) are cut into split_keys(n_q)-key splits.
 template <class F>
 RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, F rowinfo) {
   RowPlan pl;
   const int32_t split = pkv::split_keys(n_q);
   v.assign(static_cast<size_t>(M) * pkv::kRowInts, 0);
   std::vector<std::pair<int32_t, int32_t>> tails;  // (partial keys, row)
+  pl.item_off = v.size();
   for (int32_t r = 0; r < M; ++r) {
     const RowIn in = rowinfo(r);
     const int64_t own = static_cast<int64_t>(in.start) + n_q - in.k_off;
@@ -237,12 +238,14 @@ RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, F rowinfo) {
     int32_t* d = v.data() + static_cast<size_t>(r) * pkv::kRowInts;
     d[0] = in.start;
     d[1] = in.pt_off;
-    d[2] = pl.n_full;
-    d[3] = nsp;
-    d[4] = pl.n_slots + in.n_pre;
-    d[5] = in.k_off;
-    d[6] = in.n_pre;
-    pl.n_full += rem ? nsp - 1 : nsp;
+    d[2] = nsp;
+    d[3] = pl.n_slots + in.n_pre;
+    d[4] = in.k_off;
+    d[5] = in.n_pre;
+    for (int32_t sp = 0; sp < (rem ? nsp - 1 : nsp); ++sp) {
+      v.push_back(r);
+      v.push_back(sp);
+    }
     pl.n_items += nsp;
     pl.n_slots += in.n_pre + nsp;
     pl.max_parts = std::max(pl.max_parts, in.n_pre + nsp);
@@ -251,8 +254,10 @@ RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, F rowinfo) {
   std::stable_sort(tails.begin(), tails.end(),
                    [](const std::pair<int32_t, int32_t>& x,
                       const std::pair<int32_t, int32_t>& y) { return x.first > y.first; });
-  pl.tail_off = v.size();
-  for (const auto& t : tails) v.push_back(t.second);
+  for (const auto& t : tails) {
+    v.push_back(t.second);
+    v.push_back(v[static_cast<size_t>(t.second) * pkv::kRowInts + 2] - 1);
+  }
   return pl;
 }
 
@@ -536,14 +541,13 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   const int32_t group = n_heads / n_kv_heads;
   AttnArgs a;
   a.rows = reinterpret_cast<const RowDesc*>(rows_dev);
-  a.tail_rows = rows_dev + pl.tail_off;
+  a.items = reinterpret_cast<const int2*>(rows_dev + pl.item_off);
   a.Q = Q;
   a.out = out;
   a.part_o = static_cast<float*>(ws);
   a.part_ml = ws ? static_cast<float*>(ws) +
                        static_cast<size_t>(pl.n_slots) * n_q * n_heads * head_dim
                  : nullptr;
-  a.n_full_items = pl.n_full;
   a.n_rows = M;
   a.n_heads = n_heads;
   a.n_kv_heads = n_kv_heads;

@@ -8,11 +8,10 @@
 // step share it).
 //
 // Decode work items: each row's keys are cut into fixed splits (512 keys for
-// up to four new rows per sequence, 1024 beyond).  Items
-// 0 .. n_full_items-1 are the full splits, numbered row by row (the kernel
-// finds an item's row by binary search over first_full); the remaining
-// items are the rows' partial last splits, longest first (tail_rows), so the
-// end of the grid is filled with the shortest work.
+// up to four new rows per sequence, 1024 beyond).  The item list holds
+// (row, split) pairs: every row's full splits first, then the rows' partial
+// last splits, longest first, so the end of the grid is filled with the
+// shortest work.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -25,13 +24,12 @@ struct RowDesc {
   int32_t start;       // rows cached before this call (= seq_len)
   int32_t pt_off;      // paged: offset of the row's page table in the mirror;
                        // contiguous: the cache slot
-  int32_t first_full;  // decode: first full-split item of this row
   int32_t n_splits;    // decode: splits of the row's own keys, last may be partial
   int32_t part_base;   // decode: partial-result slot of own split 0
   int32_t k_off;       // first own key: keys below it form a prefix shared with
                        // other rows of the batch (shared-prefix decode), else 0
   int32_t n_pre;       // partial slots of the shared prefix, part_base - n_pre ..
-  int32_t pad;
+  int32_t pad[2];
 };
 constexpr int kRowInts = sizeof(RowDesc) / sizeof(int32_t);
 
@@ -96,12 +94,11 @@ inline bool fast_verify_ok(int32_t head_dim, int32_t group, int32_t block,
 
 struct AttnArgs {
   const RowDesc* rows;
-  const int32_t* tail_rows;  // decode: rows of the partial-split items
+  const int2* items;         // split work items: (row, split)
   const float* Q;
   float* out;
   float* part_o;      // [slots][n_q][n_heads][head_dim]   (split decode)
   float* part_ml;     // [slots][n_q][n_heads][2]
-  int32_t n_full_items;  // decode / multi-query: items before the tail items
   int32_t n_rows;
   int32_t n_heads;
   int32_t n_kv_heads;

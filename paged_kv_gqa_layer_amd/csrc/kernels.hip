@@ -263,20 +263,8 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   const int32_t G = a.n_kv_heads;
   const int32_t item_idx = blockIdx.x / G;
   const int32_t kvh = blockIdx.x - item_idx * G;
-  int32_t row, split;
-  if (item_idx < a.n_full_items) {
-    // full split: the last row with first_full <= item_idx owns it
-    int32_t lo = 0, hi = a.n_rows - 1;
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if (a.rows[mid].first_full <= item_idx) lo = mid; else hi = mid - 1;
-    }
-    row = lo;
-    split = item_idx - a.rows[row].first_full;
-  } else {
-    row = a.tail_rows[item_idx - a.n_full_items];
-    split = a.rows[row].n_splits - 1;
-  }
+  const int2 item = a.items[item_idx];
+  const int32_t row = item.x, split = item.y;
   const RowDesc rd = a.rows[row];
   const int32_t nsp = rd.n_pre + rd.n_splits;  // partial results of the row
   const int32_t slot = rd.part_base + split;
@@ -775,19 +763,8 @@ void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
   const int32_t G = a.n_kv_heads;
   const int32_t item_idx = blockIdx.x / G;
   const int32_t kvh = blockIdx.x - item_idx * G;
-  int32_t row, split;
-  if (item_idx < a.n_full_items) {
-    int32_t lo = 0, hi = a.n_rows - 1;
-    while (lo < hi) {
-      const int32_t mid = (lo + hi + 1) >> 1;
-      if (a.rows[mid].first_full <= item_idx) lo = mid; else hi = mid - 1;
-    }
-    row = lo;
-    split = item_idx - a.rows[row].first_full;
-  } else {
-    row = a.tail_rows[item_idx - a.n_full_items];
-    split = a.rows[row].n_splits - 1;
-  }
+  const int2 item = a.items[item_idx];
+  const int32_t row = item.x, split = item.y;
   const RowDesc rd = a.rows[row];
   const int32_t nsp = rd.n_pre + rd.n_splits;
   const int32_t slot = rd.part_base + split;
