@@ -996,13 +996,14 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n,
 //
 //   S^T[key][row] = sum_d K[key][d] Q[row][d]     (64 MFMAs, K=2 each)
 //   mask (offset-causal), online softmax per row
-//   O[row][d]   += sum_key P[row][key] V[key][d]  (4 x 16 MFMAs)
+//   O^T[d][row]  += sum_key V[key][d] P[row][key]  (4 x 16 MFMAs)
 //
 // 32x32 MFMA operand/result layout: lane l supplies A[l%32][l/32] and
 // B[l/32][l%32]; accumulator r of lane l is D[8*(r/4) + 4*(l/32) + r%4][l%32].
-// Computing S transposed leaves each lane with one row's scores, so the
-// softmax statistics are lane-local; the contraction index of the PV
-// product is permuted to match (key 8*(s/4) + 4*h + s%4 at step s).
+// Computing S and O transposed leaves each lane with one row's scores and
+// output, so the softmax statistics, the rescale of O and the final divide
+// are lane-local; the contraction index of the PV product is permuted to
+// match the score accumulators (key 8*(s/4) + 4*h + s%4 at step s).
 // ---------------------------------------------------------------------------
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
@@ -1158,23 +1159,25 @@ void prefill_mfma_kernel(Map m, AttnArgs a,
       ps += __shfl_xor(ps, 32);
       l_run = fmaf(l_run, alpha, ps);
       m_run = m_new;
-      // rescale O: accumulator r holds row 8*(r/4) + 4*h + r%4
+      // O^T block b (dims 32b ..) keeps row lr in this lane: the rescale is
+      // lane-local
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float ar = __shfl(alpha, 8 * (r >> 2) + 4 * h + (r & 3));
-        O0[r] *= ar;
-        O1[r] *= ar;
-        O2[r] *= ar;
-        O3[r] *= ar;
+        O0[r] *= alpha;
+        O1[r] *= alpha;
+        O2[r] *= alpha;
+        O3[r] *= alpha;
       }
+      // O^T = V^T P^T: A = V^T (lane: dim 32b + lr, key of step s), B = P^T
+      // (lane: row lr, the same key -- score accumulator s)
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const int key = 8 * (s >> 2) + 4 * h + (s & 3);
         const float* vrow = &Vs[key * VSTR + lr];
-        O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(S[s], vrow[0], O0, 0, 0, 0);
-        O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(S[s], vrow[32], O1, 0, 0, 0);
-        O2 = __builtin_amdgcn_mfma_f32_32x32x2f32(S[s], vrow[64], O2, 0, 0, 0);
-        O3 = __builtin_amdgcn_mfma_f32_32x32x2f32(S[s], vrow[96], O3, 0, 0, 0);
+        O0 = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[0], S[s], O0, 0, 0, 0);
+        O1 = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[32], S[s], O1, 0, 0, 0);
+        O2 = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[64], S[s], O2, 0, 0, 0);
+        O3 = __builtin_amdgcn_mfma_f32_32x32x2f32(vrow[96], S[s], O3, 0, 0, 0);
       }
     }
     // The other buffer was last read in iteration t-1, which ended with a
@@ -1183,19 +1186,24 @@ void prefill_mfma_kernel(Map m, AttnArgs a,
     __syncthreads();
   }
 
-  // normalise and store: accumulator r holds row 8*(r/4) + 4*h + r%4, dim 32*db + lr
+  // normalise and store: this lane holds row lr (query qi, head jh);
+  // accumulator r of block b is dim 32b + 8(r/4) + 4h + r%4
+  if (row_valid) {
+    float* op = a.out + (((int64_t)row * n_q + qi) * a.n_heads + kvh * 4 + jh) * D + 4 * h;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rowr = 8 * (r >> 2) + 4 * h + (r & 3);
-    const float lsum = __shfl(l_run, rowr);
-    const int32_t qq = q0 + 8 * w + (rowr >> 2);
-    const int32_t jj = rowr & 3;
-    if (qq < n_q) {
-      float* op = a.out + (((int64_t)row * n_q + qq) * a.n_heads + kvh * 4 + jj) * D + lr;
-      op[0] = O0[r] / lsum;
-      op[32] = O1[r] / lsum;
-      op[64] = O2[r] / lsum;
-      op[96] = O3[r] / lsum;
+    for (int g = 0; g < 4; ++g) {
+      *reinterpret_cast<float4*>(op + 8 * g) =
+          make_float4(O0[4 * g] / l_run, O0[4 * g + 1] / l_run, O0[4 * g + 2] / l_run,
+                      O0[4 * g + 3] / l_run);
+      *reinterpret_cast<float4*>(op + 32 + 8 * g) =
+          make_float4(O1[4 * g] / l_run, O1[4 * g + 1] / l_run, O1[4 * g + 2] / l_run,
+                      O1[4 * g + 3] / l_run);
+      *reinterpret_cast<float4*>(op + 64 + 8 * g) =
+          make_float4(O2[4 * g] / l_run, O2[4 * g + 1] / l_run, O2[4 * g + 2] / l_run,
+                      O2[4 * g + 3] / l_run);
+      *reinterpret_cast<float4*>(op + 96 + 8 * g) =
+          make_float4(O3[4 * g] / l_run, O3[4 * g + 1] / l_run, O3[4 * g + 2] / l_run,
+                      O3[4 * g + 3] / l_run);
     }
   }
 }
