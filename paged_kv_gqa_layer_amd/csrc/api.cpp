@@ -584,7 +584,7 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   const bool decode = kind == Kind::kDecode || kind == Kind::kDecodeShared;
   if (!decode && pkv::fast_prefill_ok(head_dim, group, block_size)) {
     DeviceCtx::ProfScope ps(&dev, PKV_K_PREFILL, st);
-    return dev_status(pkv::launch_prefill_mfma(map, a, st));
+    return dev_status(pkv::launch_prefill_mfma(map, a, group, st));
   }
   if (group > 16) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(group) * head_dim * 2 + group * 64 > 16384)

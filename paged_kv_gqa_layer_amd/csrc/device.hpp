@@ -73,8 +73,9 @@ constexpr int32_t kDecodeSplit = 512;
 // rows per kv head each key costs more work, so splits are longer and the
 // partial results fewer.
 inline int32_t split_keys(int32_t n_q) { return n_q <= 4 ? kDecodeSplit : 2 * kDecodeSplit; }
-// Queries per workgroup of the MFMA prefill kernel.
-constexpr int32_t kPrefillQTile = 32;
+// Queries per workgroup of the MFMA prefill kernel: 4 waves of 32 MFMA rows,
+// each row one (query, head of the group).
+constexpr int32_t prefill_q_tile(int32_t group) { return 128 / group; }
 
 // Kernel shapes the specialised paths cover.
 inline bool fast_decode_ok(int32_t head_dim, int32_t group, int32_t block) {
@@ -82,7 +83,8 @@ inline bool fast_decode_ok(int32_t head_dim, int32_t group, int32_t block) {
          (group == 1 || group == 2 || group == 4 || group == 8);
 }
 inline bool fast_prefill_ok(int32_t head_dim, int32_t group, int32_t block) {
-  return head_dim == 128 && block == 16 && group == 4;
+  return head_dim == 128 && block == 16 &&
+         (group == 1 || group == 2 || group == 4 || group == 8);
 }
 // Query rows (n_q x group) the split multi-query kernel holds per kv head.
 constexpr int32_t kVerifyMaxRows = 32;
@@ -160,8 +162,8 @@ hipError_t launch_generic(const PagedMap& m, const AttnArgs& a,
 hipError_t launch_generic(const ContigMap& m, const AttnArgs& a,
                           int32_t group, hipStream_t st);
 hipError_t launch_prefill_mfma(const PagedMap& m, const AttnArgs& a,
-                               hipStream_t st);
+                               int32_t group, hipStream_t st);
 hipError_t launch_prefill_mfma(const ContigMap& m, const AttnArgs& a,
-                               hipStream_t st);
+                               int32_t group, hipStream_t st);
 
 }  // namespace pkv

@@ -987,12 +987,13 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n,
 
 // ---------------------------------------------------------------------------
 // Chunked prefill on FP32 MFMA (v_mfma_f32_32x32x2_f32), head_dim 128, GQA
-// group 4, 16-row pages.
+// group GROUP in {1, 2, 4, 8}, 16-row pages.
 //
-// Workgroup = 4 waves = 32 queries of one (row, kv head).  Each wave owns 32
-// MFMA rows = 8 queries x the 4 heads of the group (row = 4*query + head), so
-// one K/V tile feeds all four heads.  Keys are processed in tiles of 32 (two
-// pages) staged in LDS by the whole workgroup.
+// Workgroup = 4 waves of one (row, kv head).  Each wave owns 32 MFMA rows =
+// 32 / GROUP queries x the GROUP heads of the group (row = GROUP*query +
+// head), so one K/V tile feeds every head of the group; a workgroup covers
+// prefill_q_tile(GROUP) = 128 / GROUP queries.  Keys are processed in tiles
+// of 32 (two pages) staged in LDS by the whole workgroup.
 //
 //   S^T[key][row] = sum_d K[key][d] Q[row][d]     (64 MFMAs, K=2 each)
 //   mask (offset-causal), online softmax per row
@@ -1007,14 +1008,13 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n,
 // ---------------------------------------------------------------------------
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-template <class Map>
+template <int GROUP, class Map>
 // Two waves per SIMD (two workgroups per CU): the register budget is capped at
 // 256 so one workgroup's MFMAs overlap the other's softmax, LDS and barriers.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_mfma_kernel(Map m, AttnArgs a,
-                                                          int32_t n_qt,
-                                                          int32_t n_wg) {
+void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
   constexpr int D = 128;
+  constexpr int QPW = 32 / GROUP;  // queries per wave
   constexpr int KT = 32;
   constexpr int KSTR = 132;  // padded LDS row strides (bank spread)
   constexpr int VSTR = 136;
@@ -1039,18 +1039,18 @@ void prefill_mfma_kernel(Map m, AttnArgs a,
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int lr = lane & 31;
-  const int32_t q0 = qt * kPrefillQTile;
+  const int32_t q0 = qt * (4 * QPW);
 
   // this lane's MFMA row
-  const int32_t qi = q0 + 8 * w + (lr >> 2);
-  const int32_t jh = lr & 3;
+  const int32_t qi = q0 + QPW * w + lr / GROUP;
+  const int32_t jh = lr % GROUP;
   const bool row_valid = qi < n_q;
   const int32_t q_pos = row_valid ? total_k - n_q + qi : total_k - 1;
 
   float4 qreg[16];
   {
     const float* qp = a.Q +
-        (((int64_t)row * n_q + (row_valid ? qi : 0)) * a.n_heads + kvh * 4 + jh) * D +
+        (((int64_t)row * n_q + (row_valid ? qi : 0)) * a.n_heads + kvh * GROUP + jh) * D +
         4 * h;
 #pragma unroll
     for (int t = 0; t < 16; ++t)
@@ -1076,11 +1076,11 @@ void prefill_mfma_kernel(Map m, AttnArgs a,
     }
   }
 
-  const int32_t q_last = min(q0 + kPrefillQTile, n_q) - 1;
+  const int32_t q_last = min(q0 + 4 * QPW, n_q) - 1;
   const int32_t kmax = a.causal ? total_k - n_q + q_last + 1 : total_k;
   const int32_t n_tiles = (kmax + KT - 1) / KT;
-  const int32_t wq_first = q0 + 8 * w;
-  const int32_t wq_last = min(q0 + 8 * w + 7, n_q - 1);
+  const int32_t wq_first = q0 + QPW * w;
+  const int32_t wq_last = min(q0 + QPW * w + QPW - 1, n_q - 1);
   const int32_t wkmax = (wq_first > wq_last)
                             ? 0
                             : (a.causal ? total_k - n_q + wq_last + 1 : total_k);
@@ -1189,7 +1189,7 @@ void prefill_mfma_kernel(Map m, AttnArgs a,
   // normalise and store: this lane holds row lr (query qi, head jh);
   // accumulator r of block b is dim 32b + 8(r/4) + 4h + r%4
   if (row_valid) {
-    float* op = a.out + (((int64_t)row * n_q + qi) * a.n_heads + kvh * 4 + jh) * D + 4 * h;
+    float* op = a.out + (((int64_t)row * n_q + qi) * a.n_heads + kvh * GROUP + jh) * D + 4 * h;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       *reinterpret_cast<float4*>(op + 8 * g) =
@@ -1286,12 +1286,25 @@ hipError_t generic_impl(const Map& m, const AttnArgs& a, int32_t group,
   return hipGetLastError();
 }
 
-template <class Map>
-hipError_t prefill_impl(const Map& m, const AttnArgs& a, hipStream_t st) {
-  const int32_t n_qt = (a.n_q + kPrefillQTile - 1) / kPrefillQTile;
+template <int GROUP, class Map>
+hipError_t prefill_group(const Map& m, const AttnArgs& a, hipStream_t st) {
+  constexpr int32_t qt = prefill_q_tile(GROUP);
+  const int32_t n_qt = (a.n_q + qt - 1) / qt;
   const int32_t n_wg = a.n_rows * a.n_kv_heads * n_qt;
-  prefill_mfma_kernel<Map><<<n_wg, 256, 0, st>>>(m, a, n_qt, n_wg);
+  prefill_mfma_kernel<GROUP, Map><<<n_wg, 256, 0, st>>>(m, a, n_qt, n_wg);
   return hipGetLastError();
+}
+
+template <class Map>
+hipError_t prefill_impl(const Map& m, const AttnArgs& a, int32_t group,
+                        hipStream_t st) {
+  switch (group) {
+    case 1: return prefill_group<1>(m, a, st);
+    case 2: return prefill_group<2>(m, a, st);
+    case 4: return prefill_group<4>(m, a, st);
+    case 8: return prefill_group<8>(m, a, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
@@ -1367,12 +1380,12 @@ hipError_t launch_generic(const ContigMap& m, const AttnArgs& a, int32_t group,
   return generic_impl(m, a, group, st);
 }
 hipError_t launch_prefill_mfma(const PagedMap& m, const AttnArgs& a,
-                               hipStream_t st) {
-  return prefill_impl(m, a, st);
+                               int32_t group, hipStream_t st) {
+  return prefill_impl(m, a, group, st);
 }
 hipError_t launch_prefill_mfma(const ContigMap& m, const AttnArgs& a,
-                               hipStream_t st) {
-  return prefill_impl(m, a, st);
+                               int32_t group, hipStream_t st) {
+  return prefill_impl(m, a, group, st);
 }
 
 }  // namespace pkv

@@ -445,3 +445,48 @@ def test_page_table_mirror_grows_after_first_use():
                                      np.concatenate([h[1], v[r:r + 1]]), H, G, D, True,
                                      scale)
         assert_close(got[r:r + 1], ref, "row %d" % r)
+
+
+@pytest.mark.parametrize("H,cached,n_q,causal", [
+    (8, 45, 130, True),     # group 1: 128 queries per workgroup, ragged second tile
+    (8, 0, 20, False),
+    (16, 300, 70, True),    # group 2: 64 per workgroup
+    (64, 17, 37, True),     # group 8: 16 per workgroup, three tiles
+    (64, 100, 16, False),
+])
+def test_prefill_mfma_other_groups_vs_oracle_and_contiguous(H, cached, n_q, causal):
+    G, D = 8, 128
+    rng = np.random.default_rng(H * 100 + n_q)
+    lens = [cached, cached + 5]
+    M = 2
+    hist = [(rng.standard_normal((l, G * D)).astype(np.float32) * 0.5,
+             rng.standard_normal((l, G * D)).astype(np.float32) * 0.5) for l in lens]
+    pool = pkv.Pool(sum((l + n_q) // 16 + 2 for l in lens), 16, 1, G, D, max_seqs=4)
+    pool.set_free_order(rng.permutation(pool.n_blocks))
+    seqs = [pool.seq_new(l + n_q) for l in lens]
+    fill_history(pool, seqs, lambda r: hist[r])
+    Q = (rng.standard_normal((M * n_q, H * D)) * 0.5).astype(np.float32)
+    K = (rng.standard_normal((M * n_q, G * D)) * 0.5).astype(np.float32)
+    V = (rng.standard_normal((M * n_q, G * D)) * 0.5).astype(np.float32)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    pool.ensure_append(seqs, n_q, check=True)
+    pool.append_layer(seqs, n_q, 0, dev(K), dev(V), check=True)
+    out = torch.full((M * n_q, H * D), float("nan"), device="cuda")
+    pool.attn_paged_prefill(seqs, n_q, 0, H, G, D, dev(Q), causal, scale, out,
+                            check=True)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for r in range(M):
+        Kc = np.concatenate([hist[r][0], K[r * n_q:(r + 1) * n_q]])
+        Vc = np.concatenate([hist[r][1], V[r * n_q:(r + 1) * n_q]])
+        rc, ref = oracle.attn_contig(Q[r * n_q:(r + 1) * n_q], Kc, Vc, H, G, D,
+                                     causal, scale)
+        assert rc == 0
+        assert_close(got[r * n_q:(r + 1) * n_q], ref, "group %d row %d" % (H // G, r))
+    cc = pkv.ContigCache(M, 1, G, max(lens) + n_q, D)
+    fill_contig(cc, [0, 1], lambda r: hist[r])
+    cc.append([0, 1], lens, n_q, 0, dev(K), dev(V))
+    cout = torch.full_like(out, float("nan"))
+    cc.attn_prefill([0, 1], lens, n_q, 0, H, dev(Q), causal, scale, cout)
+    torch.cuda.synchronize()
+    assert bits_equal(out, cout)
