@@ -120,10 +120,11 @@ struct AttnArgs {
   const int32_t* members;    // batch rows of each group, consecutive
   int32_t n_pre_items;
 };
-// Keys per split of the shared-prefix kernel (eight pages).
+// Keys per split of the shared-prefix kernel (four 32-key tiles).
 constexpr int32_t kPrefixSplit = 128;
-// Query rows per workgroup of the shared-prefix kernel (four waves of 16).
-constexpr int32_t kPrefixRows = 64;
+// Query rows per workgroup of the shared-prefix kernel (four waves of 32
+// MFMA rows).
+constexpr int32_t kPrefixRows = 128;
 
 // Launchers (kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_patch(int32_t* mirror, const int32_t* patches, int32_t n,

@@ -808,60 +808,6 @@ void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
 }
 
 // ---------------------------------------------------------------------------
-// Shared-prefix decode: the batch rows of a group share their first
-// prefix_keys keys (the same blocks, by reference count after a fork).  One
-// workgroup per (prefix item = group x kPrefixSplit keys x block of
-// kPrefixRows query rows, kv head) runs those keys once for the queries of
-// up to kPrefixRows / group members (row rho = member * group + head in
-// group) and writes each member's prefix partial result.  Every prefix key
-// precedes each member's new row, so nothing is masked.
-// ---------------------------------------------------------------------------
-template <class Map>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefix_mfma_kernel(Map m, AttnArgs a, int32_t group) {
-  constexpr int D = 128;
-  constexpr int NB = kPrefixRows / 16;
-  __shared__ MqLds<NB> sh;
-  const int32_t G = a.n_kv_heads;
-  const int32_t item_idx = blockIdx.x / G;
-  const int32_t kvh = blockIdx.x - item_idx * G;
-  const int4 it = reinterpret_cast<const int4*>(a.pre_items)[item_idx];
-  const int4 gd = reinterpret_cast<const int4*>(a.groups)[it.x];
-  const int32_t split = it.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int mq = lane >> 4;
-  const int32_t k_begin = split * kPrefixSplit;
-  const int32_t k_end = min(gd.w, k_begin + kPrefixSplit);
-
-  const int32_t rho = kPrefixRows * it.z + 16 * wave + (lane & 15);
-  const bool valid = rho < gd.z * group;
-  const int32_t mi = valid ? rho / group : 0;
-  const int32_t hj = valid ? rho - mi * group : 0;
-  const int32_t row = a.members[gd.y + mi];
-  const RowDesc rd = a.rows[row];
-  const int64_t qrow = (int64_t)row * a.n_heads + (int64_t)kvh * group + hj;
-  float4 qv[8];
-  mq_load_q(a.Q + qrow * D, valid, mq, a.rope, rd.start, a.qscale, qv);
-
-  floatx4 Ot[8];
-#pragma unroll
-  for (int b = 0; b < 8; ++b) Ot[b] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
-  mq_attend<NB>(m, a.rows[gd.x], kvh, k_begin, k_end, INT32_MAX, qv, Ot, m_run,
-                l_run, sh);
-
-  if (!valid) return;
-  const int64_t e = (int64_t)(rd.part_base - rd.n_pre + split) * a.n_heads +
-                    kvh * group + hj;
-  mq_store_partial(a.part_o + e * D, mq, Ot);
-  if (mq == 0) {
-    a.part_ml[e * 2 + 0] = m_run;
-    a.part_ml[e * 2 + 1] = l_run;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Generic attention (any head_dim, group, page size; decode or prefill): one
 // wave per (query row, kv head) over all its visible keys.  Lanes take 64
 // keys at a time for the scores; for the weighted sum they take dims.
@@ -1008,7 +954,15 @@ __global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n,
 // ---------------------------------------------------------------------------
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-template <int GROUP, class Map>
+// PREFIX = true is the shared-prefix form of the same kernel (shared-prefix
+// decode): one workgroup per (prefix item = group x kPrefixSplit prefix keys
+// x block of 128 query rows, kv head); its MFMA rows are (member, head)
+// pairs of the group's members -- the batch rows that share the prefix, one
+// new query each -- over the prefix keys of the split, read through the
+// first member's page table; nothing is masked (every prefix key precedes
+// each member's new row) and each row's unnormalised state goes to its
+// prefix partial slot for merge_kernel.
+template <int GROUP, bool PREFIX, class Map>
 // Two waves per SIMD (two workgroups per CU): the register budget is capped at
 // 256 so one workgroup's MFMAs overlap the other's softmax, LDS and barriers.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1022,42 +976,75 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
   __shared__ float Ks2[2][KT * KSTR];
   __shared__ float Vs2[2][KT * VSTR];
 
-  // Keep all query tiles of one (row, kv head) on one XCD (they share K/V).
-  const int32_t b = blockIdx.x;
-  const int32_t Lw = (n_wg % 8 == 0) ? (b % 8) * (n_wg / 8) + b / 8 : b;
-  const int32_t G = a.n_kv_heads;
-  const int32_t row = Lw / (G * n_qt);
-  const int32_t rem = Lw - row * G * n_qt;
-  const int32_t kvh = rem / n_qt;
-  const int32_t qt = rem - kvh * n_qt;
-  const RowDesc rd = a.rows[row];
-  const int32_t total_k = rd.start + a.n_q;
-  const int32_t n_q = a.n_q;
-
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int lane = tid & 63;
   const int h = lane >> 5;
   const int lr = lane & 31;
-  const int32_t q0 = qt * (4 * QPW);
+  const int32_t G = a.n_kv_heads;
+  const int32_t jh = lr % GROUP;  // head of the group of this lane's MFMA row
 
-  // this lane's MFMA row
-  const int32_t qi = q0 + QPW * w + lr / GROUP;
-  const int32_t jh = lr % GROUP;
-  const bool row_valid = qi < n_q;
-  const int32_t q_pos = row_valid ? total_k - n_q + qi : total_k - 1;
+  // What this workgroup runs: the pages of rd for kv head kvh, keys
+  // [k_first, k_lim); this lane's query row (q_row indexes Q and out rows,
+  // q_pos is its position, keys above mask_pos are masked); the keys wave w
+  // needs at all (w_lim).
+  RowDesc rd;
+  int32_t kvh, k_first, k_lim, q_row, q_pos, mask_pos, w_lim;
+  bool row_valid;
+  int64_t slot = 0;  // PREFIX: the row's partial slot
+  if constexpr (!PREFIX) {
+    // Keep all query tiles of one (row, kv head) on one XCD (they share K/V).
+    const int32_t b = blockIdx.x;
+    const int32_t Lw = (n_wg % 8 == 0) ? (b % 8) * (n_wg / 8) + b / 8 : b;
+    const int32_t row = Lw / (G * n_qt);
+    const int32_t rem = Lw - row * G * n_qt;
+    kvh = rem / n_qt;
+    const int32_t qt = rem - kvh * n_qt;
+    rd = a.rows[row];
+    const int32_t n_q = a.n_q;
+    const int32_t total_k = rd.start + n_q;
+    const int32_t q0 = qt * (4 * QPW);
+    const int32_t qi = q0 + QPW * w + lr / GROUP;
+    row_valid = qi < n_q;
+    q_pos = row_valid ? total_k - n_q + qi : total_k - 1;
+    q_row = row * n_q + (row_valid ? qi : 0);
+    mask_pos = a.causal ? q_pos : INT32_MAX;
+    k_first = 0;
+    const int32_t q_last = min(q0 + 4 * QPW, n_q) - 1;
+    k_lim = a.causal ? total_k - n_q + q_last + 1 : total_k;
+    const int32_t wq_first = q0 + QPW * w;
+    const int32_t wq_last = min(q0 + QPW * w + QPW - 1, n_q - 1);
+    w_lim = (wq_first > wq_last) ? 0 : (a.causal ? total_k - n_q + wq_last + 1 : total_k);
+  } else {
+    const int32_t item = blockIdx.x / G;
+    kvh = blockIdx.x - item * G;
+    const int4 it = reinterpret_cast<const int4*>(a.pre_items)[item];
+    const int4 gd = reinterpret_cast<const int4*>(a.groups)[it.x];
+    k_first = it.y * kPrefixSplit;
+    k_lim = min(gd.w, k_first + kPrefixSplit);
+    const int32_t m0 = it.z * (4 * QPW);
+    const int32_t mi = m0 + QPW * w + lr / GROUP;
+    row_valid = mi < gd.z;
+    const int32_t mrow = a.members[gd.y + (row_valid ? mi : 0)];
+    const RowDesc md = a.rows[mrow];
+    rd = a.rows[gd.x];
+    q_row = mrow;
+    q_pos = md.start;
+    mask_pos = INT32_MAX;
+    w_lim = (m0 + QPW * w < gd.z) ? k_lim : 0;
+    slot = md.part_base - md.n_pre + it.y;
+  }
 
   float4 qreg[16];
   {
-    const float* qp = a.Q +
-        (((int64_t)row * n_q + (row_valid ? qi : 0)) * a.n_heads + kvh * GROUP + jh) * D +
-        4 * h;
+    const float* qp =
+        a.Q + ((int64_t)q_row * a.n_heads + kvh * GROUP + jh) * D + 4 * h;
 #pragma unroll
     for (int t = 0; t < 16; ++t)
       qreg[t] = row_valid ? ld4(qp + 8 * t) : make_float4(0.f, 0.f, 0.f, 0.f);
     if (a.rope) {
       // qreg[t] holds dims 8t+4h .. 8t+4h+3; for t < 8 they pair with
-      // qreg[t + 8] (dims + 64).  Rows past n_q hold zeros and stay zero.
+      // qreg[t + 8] (dims + 64).  Invalid rows hold zeros and stay zero.
       const double2* cr = a.rope + (int64_t)q_pos * (D / 2) + 4 * h;
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -1076,14 +1063,8 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
     }
   }
 
-  const int32_t q_last = min(q0 + 4 * QPW, n_q) - 1;
-  const int32_t kmax = a.causal ? total_k - n_q + q_last + 1 : total_k;
-  const int32_t n_tiles = (kmax + KT - 1) / KT;
-  const int32_t wq_first = q0 + QPW * w;
-  const int32_t wq_last = min(q0 + QPW * w + QPW - 1, n_q - 1);
-  const int32_t wkmax = (wq_first > wq_last)
-                            ? 0
-                            : (a.causal ? total_k - n_q + wq_last + 1 : total_k);
+  const int32_t t_first = k_first / KT;
+  const int32_t n_tiles = (k_lim + KT - 1) / KT;
 
   floatx16 O0 = {}, O1 = {}, O2 = {}, O3 = {};
   float m_run = kNegInf;
@@ -1097,13 +1078,13 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
     const int32_t k0 = t * KT;
     const int32_t pg = k0 / 16;
     const float* p0 = m.page(rd, pg, kvh);
-    const float* p1 = (k0 + 16 < total_k) ? m.page(rd, pg + 1, kvh) : p0;
+    const float* p1 = (k0 + 16 < k_lim) ? m.page(rd, pg + 1, kvh) : p0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int key = ld_key + 8 * u;
       const float* base = (u < 2) ? p0 : p1;
       const int off = (key & 15) * D + ld_c;
-      if (k0 + key < total_k) {
+      if (k0 + key < k_lim) {
         kr[u] = ld4(base + off);
         vr[u] = ld4(base + m.v_off + off);
       } else {
@@ -1120,15 +1101,16 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
     }
   };
 
-  load_tile(0);
+  load_tile(t_first);
   store_tile(0);
   __syncthreads();
-  for (int32_t t = 0; t < n_tiles; ++t) {
+  for (int32_t t = t_first; t < n_tiles; ++t) {
+    const int buf = (t - t_first) & 1;
     if (t + 1 < n_tiles) load_tile(t + 1);
-    const float* Ks = Ks2[t & 1];
-    const float* Vs = Vs2[t & 1];
+    const float* Ks = Ks2[buf];
+    const float* Vs = Vs2[buf];
     const int32_t k0 = t * KT;
-    if (k0 < wkmax) {
+    if (k0 < w_lim) {
       floatx16 S = {};
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
@@ -1143,12 +1125,12 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int32_t key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const bool vis = a.causal ? (key <= q_pos) : (key < total_k);
-        if (!vis) S[r] = kNegInf;
+        if (!(key < k_lim && key <= mask_pos)) S[r] = kNegInf;
         mx = fmaxf(mx, S[r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);  // finite: key 0 is seen in tile 0
+      // finite: every row sees key k_first (causal rows see key 0 onwards)
+      const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - m_new);
       float ps = 0.f;
 #pragma unroll
@@ -1182,29 +1164,32 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
     }
     // The other buffer was last read in iteration t-1, which ended with a
     // barrier, so it can be refilled now; one barrier per tile.
-    if (t + 1 < n_tiles) store_tile((t + 1) & 1);
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
     __syncthreads();
   }
 
-  // normalise and store: this lane holds row lr (query qi, head jh);
-  // accumulator r of block b is dim 32b + 8(r/4) + 4h + r%4
-  if (row_valid) {
-    float* op = a.out + (((int64_t)row * n_q + qi) * a.n_heads + kvh * GROUP + jh) * D + 4 * h;
+  // Store: this lane holds row lr (query or member, head jh); accumulator r
+  // of block b is dim 32b + 8(r/4) + 4h + r%4.  Prefill divides by the row
+  // sum; the prefix form writes the unnormalised state of its key range.
+  if (!row_valid) return;
+  const int64_t e = PREFIX ? slot * a.n_heads + kvh * GROUP + jh
+                           : (int64_t)q_row * a.n_heads + kvh * GROUP + jh;
+  float* op = (PREFIX ? a.part_o : a.out) + e * D + 4 * h;
+  const float L = PREFIX ? 1.f : l_run;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      *reinterpret_cast<float4*>(op + 8 * g) =
-          make_float4(O0[4 * g] / l_run, O0[4 * g + 1] / l_run, O0[4 * g + 2] / l_run,
-                      O0[4 * g + 3] / l_run);
-      *reinterpret_cast<float4*>(op + 32 + 8 * g) =
-          make_float4(O1[4 * g] / l_run, O1[4 * g + 1] / l_run, O1[4 * g + 2] / l_run,
-                      O1[4 * g + 3] / l_run);
-      *reinterpret_cast<float4*>(op + 64 + 8 * g) =
-          make_float4(O2[4 * g] / l_run, O2[4 * g + 1] / l_run, O2[4 * g + 2] / l_run,
-                      O2[4 * g + 3] / l_run);
-      *reinterpret_cast<float4*>(op + 96 + 8 * g) =
-          make_float4(O3[4 * g] / l_run, O3[4 * g + 1] / l_run, O3[4 * g + 2] / l_run,
-                      O3[4 * g + 3] / l_run);
-    }
+  for (int g = 0; g < 4; ++g) {
+    *reinterpret_cast<float4*>(op + 8 * g) =
+        make_float4(O0[4 * g] / L, O0[4 * g + 1] / L, O0[4 * g + 2] / L, O0[4 * g + 3] / L);
+    *reinterpret_cast<float4*>(op + 32 + 8 * g) =
+        make_float4(O1[4 * g] / L, O1[4 * g + 1] / L, O1[4 * g + 2] / L, O1[4 * g + 3] / L);
+    *reinterpret_cast<float4*>(op + 64 + 8 * g) =
+        make_float4(O2[4 * g] / L, O2[4 * g + 1] / L, O2[4 * g + 2] / L, O2[4 * g + 3] / L);
+    *reinterpret_cast<float4*>(op + 96 + 8 * g) =
+        make_float4(O3[4 * g] / L, O3[4 * g + 1] / L, O3[4 * g + 2] / L, O3[4 * g + 3] / L);
+  }
+  if (PREFIX && h == 0) {
+    a.part_ml[e * 2 + 0] = m_run;
+    a.part_ml[e * 2 + 1] = l_run;
   }
 }
 
@@ -1266,8 +1251,14 @@ template <class Map>
 hipError_t prefix_impl(const Map& m, const AttnArgs& a, int32_t group,
                        hipStream_t st) {
   if (a.n_pre_items <= 0) return hipSuccess;
-  prefix_mfma_kernel<Map><<<a.n_pre_items * a.n_kv_heads, kPrefixRows / 16 * 64, 0, st>>>(
-      m, a, group);
+  const dim3 grid(a.n_pre_items * a.n_kv_heads);
+  switch (group) {
+    case 1: prefill_mfma_kernel<1, true, Map><<<grid, 256, 0, st>>>(m, a, 0, 0); break;
+    case 2: prefill_mfma_kernel<2, true, Map><<<grid, 256, 0, st>>>(m, a, 0, 0); break;
+    case 4: prefill_mfma_kernel<4, true, Map><<<grid, 256, 0, st>>>(m, a, 0, 0); break;
+    case 8: prefill_mfma_kernel<8, true, Map><<<grid, 256, 0, st>>>(m, a, 0, 0); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1291,7 +1282,7 @@ hipError_t prefill_group(const Map& m, const AttnArgs& a, hipStream_t st) {
   constexpr int32_t qt = prefill_q_tile(GROUP);
   const int32_t n_qt = (a.n_q + qt - 1) / qt;
   const int32_t n_wg = a.n_rows * a.n_kv_heads * n_qt;
-  prefill_mfma_kernel<GROUP, Map><<<n_wg, 256, 0, st>>>(m, a, n_qt, n_wg);
+  prefill_mfma_kernel<GROUP, false, Map><<<n_wg, 256, 0, st>>>(m, a, n_qt, n_wg);
   return hipGetLastError();
 }
 
