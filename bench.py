@@ -324,10 +324,11 @@ def bench_forked(args, synth, pkv, shared):
     inputs = [tuple(torch.from_numpy(a).cuda() for a in x)
               for x in synth.parallel_map(step_inputs, range(wl.steps))]
     out = torch.empty((F, H * D), device="cuda")
-    # partial slots per row: at most the prefix in 128-key splits plus the
-    # row's own keys in 512-key splits (plain decode needs fewer)
-    slots = math.ceil(wl.prefix / 128) + math.ceil((wl.steps + 1) / 512) + 1
-    ws = torch.empty(F * slots * H * (D + 2) * 4, dtype=torch.uint8, device="cuda")
+    # workspace: the library's own count for this batch, doubled for the
+    # rows the forks add over the steps (a few more 512-key splits at most)
+    ws_bytes = max(pool.decode_workspace_bytes(seqs_np, H),
+                   pool.decode_shared_workspace_bytes(seqs_np, H))
+    ws = torch.empty(2 * ws_bytes + 4, dtype=torch.uint8, device="cuda")
 
     attn = pool.attn_paged_decode_shared if shared else pool.attn_paged_decode
 
