@@ -524,7 +524,8 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 // of key 4r + m -- the key PV step r needs from that lane.
 // One wave keeps V in registers and only K in LDS (no barrier: a wave's LDS
 // accesses are in order).  Several waves split each page's loads and share K
-// and V through double-buffered LDS tiles, one barrier per page.
+// and V through one LDS tile: a barrier after the tile is read, the next page
+// stored, a barrier before it is read.
 // ---------------------------------------------------------------------------
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
@@ -535,10 +536,13 @@ __device__ __forceinline__ float f4_at(const float4& v, int e) {
 constexpr int kMqKS = 132;  // padded LDS row strides of the K / V tiles
 constexpr int kMqVS = 136;
 
+// One K tile (and, for several waves, one V tile) per workgroup: a single
+// buffer keeps the two-wave form at 17 KB, so three such workgroups fit a CU
+// beside their registers.
 template <int NB>
 struct MqLds {
-  float K[NB == 1 ? 1 : 2][16 * kMqKS];
-  float V[NB == 1 ? 1 : 2][NB == 1 ? 4 : 16 * kMqVS];
+  float K[1][16 * kMqKS];
+  float V[1][NB == 1 ? 4 : 16 * kMqVS];
 };
 
 // Q operand of one row: qp points at the row's head vector; dims
@@ -708,17 +712,22 @@ __device__ __forceinline__ void mq_attend(const Map& m, const RowDesc& rd,
     store_part(0);
     __syncthreads();
     for (int32_t p = p_begin; p < p_end; ++p) {
-      const int buf = (p - p_begin) & 1;
       if (p + 1 < p_end) load_rows(p + 1, NI * wave, kA, kB, vA, vB);
-      floatx4 S = scores(sh.K[buf]);
+      floatx4 S = scores(sh.K[0]);
       softmax_page(S, p);
-      const float* Vt = sh.V[buf];
+      // take this page's V operands, then let the tile be refilled with the
+      // next page while the PV products run
+      const float* Vt = sh.V[0];
+      float4 vva[4], vvb[4];
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2)
-        pv_step(S, s2, *reinterpret_cast<const float4*>(&Vt[(4 * s2 + mq) * VS + 4 * c16]),
-                *reinterpret_cast<const float4*>(&Vt[(4 * s2 + mq) * VS + 64 + 4 * c16]));
-      // the other buffer was last read before the previous barrier
-      if (p + 1 < p_end) store_part(buf ^ 1);
+      for (int s2 = 0; s2 < 4; ++s2) {
+        vva[s2] = *reinterpret_cast<const float4*>(&Vt[(4 * s2 + mq) * VS + 4 * c16]);
+        vvb[s2] = *reinterpret_cast<const float4*>(&Vt[(4 * s2 + mq) * VS + 64 + 4 * c16]);
+      }
+      __syncthreads();
+      if (p + 1 < p_end) store_part(0);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) pv_step(S, s2, vva[s2], vvb[s2]);
       __syncthreads();
     }
   }
@@ -756,7 +765,8 @@ __device__ __forceinline__ void mq_store_partial(float* dst, int mq,
 // query * group + head in group), NB = 1 or 2 waves of 16 rows.
 // ---------------------------------------------------------------------------
 template <int NB, class Map>
-__global__ __launch_bounds__(64 * NB) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * NB)
+__attribute__((amdgpu_waves_per_eu(NB == 1 ? 2 : 3, NB == 1 ? 2 : 3)))
 void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
   constexpr int D = 128;
   __shared__ MqLds<NB> sh;
