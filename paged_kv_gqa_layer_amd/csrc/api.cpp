@@ -217,6 +217,7 @@ struct RowPlan {
 // own key and prefix partial slots (both 0 unless a shared prefix is used).
 struct RowIn {
   int32_t start = 0, pt_off = 0, k_off = 0, n_pre = 0;
+  int32_t append_block = -1;  // paged: block of page start / block_size
 };
 
 // Row blob: RowDesc[M], then the split items as (row, split) pairs -- every
@@ -242,6 +243,7 @@ RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, F rowinfo) {
     d[3] = pl.n_slots + in.n_pre;
     d[4] = in.k_off;
     d[5] = in.n_pre;
+    d[6] = in.append_block;
     for (int32_t sp = 0; sp < (rem ? nsp - 1 : nsp); ++sp) {
       v.push_back(r);
       v.push_back(sp);
@@ -422,7 +424,8 @@ hipError_t size_mirror(pkv_pool* p, hipStream_t st) {
 // at this pool version (no patches can be pending then: every page-table
 // change bumps the version).
 hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
-                     int32_t shared_heads, hipStream_t st, const int32_t** rows_dev) {
+                     int32_t shared_heads, hipStream_t st, const int32_t** rows_dev,
+                     pkv::PatchArgs* deferred = nullptr) {
   hipError_t e = size_mirror(p, st);
   if (e != hipSuccess) return e;
   std::vector<int64_t> key;
@@ -436,10 +439,14 @@ hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
   if (key != p->rows_key || !pt.empty()) {
     const bool shared = shared_heads > 0;
     if (shared) find_shared(p->meta, seqs, M, shared_heads, &p->shared);
+    const int32_t B = p->meta.block_size();
     p->plan = build_rows(p->rows, M, n, [&](int32_t r) {
+      const pkv::SeqMeta* q = p->meta.seq(seqs[r]);
       RowIn in;
-      in.start = p->meta.seq(seqs[r])->seq_len;
+      in.start = q->seq_len;
       in.pt_off = static_cast<int32_t>(seqs[r] * p->stride);
+      const size_t pg = static_cast<size_t>(q->seq_len / B);
+      in.append_block = pg < q->pages.size() ? static_cast<int32_t>(q->pages[pg]) : -1;
       if (shared) {
         in.k_off = p->shared.k_off[r];
         in.n_pre = p->shared.n_pre[r];
@@ -464,11 +471,15 @@ hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
   const int32_t n_patch = static_cast<int32_t>((p->rows.size() - p->patch_off) / 3);
   int32_t* d = nullptr;
   if ((e = p->dev.upload(kRows, p->rows, key, st, &d)) != hipSuccess) return e;
+  if (deferred) *deferred = pkv::PatchArgs{p->mirror, d + p->patch_off, 0, p->stride};
   if (!pt.empty()) {
     pt.clear();
-    if ((e = pkv::launch_patch(p->mirror, d + p->patch_off, n_patch, p->stride, st)) !=
-        hipSuccess)
+    if (deferred) {
+      deferred->n = n_patch;  // the caller's launch applies them
+    } else if ((e = pkv::launch_patch(p->mirror, d + p->patch_off, n_patch, p->stride,
+                                      st)) != hipSuccess) {
       return e;
+    }
   }
   p->rows_key = key;
   *rows_dev = d;
@@ -794,14 +805,23 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   // groups or not, as the last attention call), so both share one upload
   const int32_t shared_heads =
       pool->last_shared && n_new == 1 ? pool->shared_heads : 0;
-  if (pool_rows(pool, seqs, M, n_new, shared_heads, st, &rows) != hipSuccess)
+  // one row per sequence: the rows name the blocks they land in, so the
+  // append kernel also applies the pending page-table patches
+  pkv::PatchArgs pa{};
+  if (pool_rows(pool, seqs, M, n_new, shared_heads, st, &rows,
+                n_new == 1 ? &pa : nullptr) != hipSuccess)
     return PKV_ERR_DEVICE;
   const PagedMap pm = make_paged_map(pool, layer);
+  const int32_t kv_dim = pool->meta.n_kv_heads() * pool->meta.head_dim();
   DeviceCtx::ProfScope ps(&pool->dev, PKV_K_APPEND, st);
+  if (n_new == 1)
+    return dev_status(pkv::launch_append_one(pm, reinterpret_cast<const RowDesc*>(rows),
+                                             K_new_dev, V_new_dev, M, kv_dim,
+                                             pool->meta.head_dim(), rope_table(pool->rope),
+                                             pa, st));
   return dev_status(pkv::launch_append(
       pm, reinterpret_cast<const RowDesc*>(rows), K_new_dev, V_new_dev, M, n_new,
-      pool->meta.n_kv_heads() * pool->meta.head_dim(), pool->meta.head_dim(),
-      rope_table(pool->rope), st));
+      kv_dim, pool->meta.head_dim(), rope_table(pool->rope), st));
 }
 
 int32_t pkv_advance(pkv_pool* pool, const int32_t* seqs, int32_t M, int32_t n) {

@@ -29,7 +29,9 @@ struct RowDesc {
   int32_t k_off;       // first own key: keys below it form a prefix shared with
                        // other rows of the batch (shared-prefix decode), else 0
   int32_t n_pre;       // partial slots of the shared prefix, part_base - n_pre ..
-  int32_t pad[2];
+  int32_t append_block;  // paged: block of page start / block_size (where a
+                         // one-row append lands), -1 if not yet reserved
+  int32_t pad;
 };
 constexpr int kRowInts = sizeof(RowDesc) / sizeof(int32_t);
 
@@ -44,10 +46,12 @@ struct PagedMap {
   int64_t head_stride;   // floats between kv heads
   int64_t v_off;         // floats from the K part to the V part
   int32_t block_size;
+  __device__ __forceinline__ float* block(int64_t b, int32_t kvh) const {
+    return base + b * block_stride + layer_off + kvh * head_stride;
+  }
   __device__ __forceinline__ float* page(const RowDesc& rd, int32_t p,
                                          int32_t kvh) const {
-    const int64_t b = pages[rd.pt_off + p];
-    return base + b * block_stride + layer_off + kvh * head_stride;
+    return block(pages[rd.pt_off + p], kvh);
   }
 };
 
@@ -140,6 +144,21 @@ hipError_t launch_append(const ContigMap& m, const RowDesc* rows,
                          const float* K, const float* V, int32_t M, int32_t n,
                          int32_t kv_dim, int32_t head_dim, const double2* rope,
                          hipStream_t st);
+// Page-table mirror patches (seq, page, block triples) applied by a launch.
+struct PatchArgs {
+  int32_t* mirror;
+  const int32_t* patches;
+  int32_t n;
+  int64_t stride;
+};
+// One new row per sequence, written to each RowDesc's append_block, with the
+// pending mirror patches applied by the same launch (the append does not
+// read the mirror).
+hipError_t launch_append_one(const PagedMap& m, const RowDesc* rows,
+                             const float* K, const float* V, int32_t M,
+                             int32_t kv_dim, int32_t head_dim,
+                             const double2* rope, const PatchArgs& pa,
+                             hipStream_t st);
 hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,
                       int64_t block_floats, hipStream_t st);
 hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,

@@ -15,6 +15,8 @@
 // softmax uses exp2; the split merge uses the same units.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "device.hpp"
 
 namespace pkv {
@@ -104,13 +106,20 @@ __device__ __forceinline__ void rotate_pair(float& lo, float& hi,
 // of a head and the VEC floats they pair with in the second half, and turns
 // the K pairs by the row's position before storing them (V is stored as is).
 // ---------------------------------------------------------------------------
-template <int VEC, class Map, bool ROPE>
+// ONE: one new row per sequence, written to the RowDesc's append_block (no
+// page-table read), while the first threads apply the pending mirror patches.
+template <int VEC, class Map, bool ROPE, bool ONE>
 __global__ __launch_bounds__(256) void append_kernel(
     Map m, const RowDesc* __restrict__ rows, const float* __restrict__ K,
     const float* __restrict__ V, int32_t n, int32_t kv_dim, int32_t head_dim,
-    int64_t total, const double2* __restrict__ cs) {
+    int64_t total, const double2* __restrict__ cs, PatchArgs pa) {
   const int32_t span = ROPE ? head_dim / 2 : head_dim;  // floats per head unit
   const int32_t per_row = (ROPE ? kv_dim / 2 : kv_dim) / VEC;
+  if constexpr (ONE) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < pa.n)
+      pa.mirror[pa.patches[3 * i] * pa.stride + pa.patches[3 * i + 1]] = pa.patches[3 * i + 2];
+  }
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t rt = e / per_row;
@@ -121,8 +130,10 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int32_t pos = rd.start + t;
     const int32_t kvh = c / span;
     const int32_t d = c - kvh * span;
-    float* dst = m.page(rd, pos / m.block_size, kvh) +
-                 (int64_t)(pos % m.block_size) * head_dim + d;
+    float* pg;
+    if constexpr (ONE) pg = m.block(rd.append_block, kvh);
+    else pg = m.page(rd, pos / m.block_size, kvh);
+    float* dst = pg + (int64_t)(pos % m.block_size) * head_dim + d;
     const int64_t src = rt * kv_dim + (int64_t)kvh * head_dim + d;
     if constexpr (ROPE) {
       const int32_t half = span;
@@ -1203,29 +1214,31 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
   }
 }
 
-template <class Map>
+template <class Map, bool ONE>
 hipError_t append_impl(const Map& m, const RowDesc* rows, const float* K,
                        const float* V, int32_t M, int32_t n, int32_t kv_dim,
-                       int32_t head_dim, const double2* cs, hipStream_t st) {
+                       int32_t head_dim, const double2* cs, const PatchArgs& pa,
+                       hipStream_t st) {
   const bool rope = cs != nullptr;
   if (rope && head_dim % 2 != 0) return hipErrorInvalidValue;
   const int32_t span = rope ? head_dim / 2 : head_dim;
   const bool vec = (span % 4 == 0);
   const int64_t total = (int64_t)M * n * (rope ? kv_dim / 2 : kv_dim) / (vec ? 4 : 1);
-  const int64_t want = (total + 255) / 256;
+  const int64_t want = (std::max<int64_t>(total, pa.n) + 255) / 256;
   const int grid = static_cast<int>(want < 65536 ? (want > 0 ? want : 1) : 65536);
+  if (ONE && (int64_t)grid * 256 < pa.n) return hipErrorInvalidValue;
   if (rope && vec)
-    append_kernel<4, Map, true><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
-                                                      head_dim, total, cs);
+    append_kernel<4, Map, true, ONE><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
+                                                           head_dim, total, cs, pa);
   else if (rope)
-    append_kernel<1, Map, true><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
-                                                      head_dim, total, cs);
+    append_kernel<1, Map, true, ONE><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
+                                                           head_dim, total, cs, pa);
   else if (vec)
-    append_kernel<4, Map, false><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
-                                                       head_dim, total, cs);
+    append_kernel<4, Map, false, ONE><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
+                                                            head_dim, total, cs, pa);
   else
-    append_kernel<1, Map, false><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
-                                                       head_dim, total, cs);
+    append_kernel<1, Map, false, ONE><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
+                                                            head_dim, total, cs, pa);
   return hipGetLastError();
 }
 
@@ -1327,13 +1340,23 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
 hipError_t launch_append(const PagedMap& m, const RowDesc* rows, const float* K,
                          const float* V, int32_t M, int32_t n, int32_t kv_dim,
                          int32_t head_dim, const double2* rope, hipStream_t st) {
-  return append_impl(m, rows, K, V, M, n, kv_dim, head_dim, rope, st);
+  return append_impl<PagedMap, false>(m, rows, K, V, M, n, kv_dim, head_dim, rope,
+                                      PatchArgs{}, st);
 }
 hipError_t launch_append(const ContigMap& m, const RowDesc* rows,
                          const float* K, const float* V, int32_t M, int32_t n,
                          int32_t kv_dim, int32_t head_dim, const double2* rope,
                          hipStream_t st) {
-  return append_impl(m, rows, K, V, M, n, kv_dim, head_dim, rope, st);
+  return append_impl<ContigMap, false>(m, rows, K, V, M, n, kv_dim, head_dim, rope,
+                                       PatchArgs{}, st);
+}
+hipError_t launch_append_one(const PagedMap& m, const RowDesc* rows,
+                             const float* K, const float* V, int32_t M,
+                             int32_t kv_dim, int32_t head_dim,
+                             const double2* rope, const PatchArgs& pa,
+                             hipStream_t st) {
+  return append_impl<PagedMap, true>(m, rows, K, V, M, 1, kv_dim, head_dim, rope, pa,
+                                     st);
 }
 
 hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,
