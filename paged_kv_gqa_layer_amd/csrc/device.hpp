@@ -133,7 +133,6 @@ constexpr int32_t kPrefixRows = 128;
 // Launchers (kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_patch(int32_t* mirror, const int32_t* patches, int32_t n,
                         int64_t stride, hipStream_t st);
-hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
 // rope: rotary table (as AttnArgs::rope) or null; K rows are turned at
 // their positions before they are stored.
 hipError_t launch_append(const PagedMap& m, const RowDesc* rows,

@@ -945,13 +945,6 @@ __global__ __launch_bounds__(256) void patch_kernel(int32_t* mirror,
   if (i < n) mirror[p[3 * i] * stride + p[3 * i + 1]] = p[3 * i + 2];
 }
 
-__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* p, int64_t n,
-                                                       int32_t v) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
-
 // ---------------------------------------------------------------------------
 // Chunked prefill on FP32 MFMA (v_mfma_f32_32x32x2_f32), head_dim 128, GQA
 // group GROUP in {1, 2, 4, 8}, 16-row pages.
@@ -1330,12 +1323,6 @@ hipError_t launch_patch(int32_t* mirror, const int32_t* patches, int32_t n,
   return hipGetLastError();
 }
 
-hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  const int64_t want = (n + 255) / 256;
-  fill_i32_kernel<<<static_cast<unsigned>(want < 4096 ? want : 4096), 256, 0, st>>>(p, n, v);
-  return hipGetLastError();
-}
 
 hipError_t launch_append(const PagedMap& m, const RowDesc* rows, const float* K,
                          const float* V, int32_t M, int32_t n, int32_t kv_dim,
