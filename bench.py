@@ -42,6 +42,13 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def pct(x):
+    """p10 / median / p90 of a list of durations."""
+    a = np.asarray(x, np.float64)
+    return {"p10": float(np.percentile(a, 10)), "p50": float(np.median(a)),
+            "p90": float(np.percentile(a, 90))}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -53,8 +60,8 @@ def parse():
     ap.add_argument("--no-verify", action="store_true")
     ap.add_argument("--no-forked", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="budget for the oracle sample")
+    ap.add_argument("--cpu-keys", type=int, default=700000,
+                    help="keys in the oracle sample (first sequences of the workload)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (calibrates the "
@@ -185,12 +192,17 @@ def bench_decode(args, synth, pkv):
             step(t)
         torch.cuda.synchronize()
         pool.profile_enable(True)
+        # per-step GPU time: events on the stream the library is given
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for t in range(t_first + args.warmup, t_first + n_steps):
+        ev[0].record()
+        for i, t in enumerate(range(t_first + args.warmup, t_first + n_steps)):
             step(t)
+            ev[i + 1].record()
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
         kv_bytes = 0
         for t in range(t_first + args.warmup, t_first + n_steps):
             kv_bytes += int((wl.ctx.astype(np.int64) + t + 1).sum()) * 2 * wl.kv_dim * 4
@@ -199,10 +211,12 @@ def bench_decode(args, synth, pkv):
                           ("merge", pkv.K_MERGE), ("cow", pkv.K_COW)):
             ms, n = pool.profile_read(kid)
             kern[name] = {"launches": n, "avg_us": (1e3 * ms / n) if n else 0.0}
+        dec_us = 1e3 * pool.profile_samples(pkv.K_DECODE)
         pool.profile_enable(False)
         dec_s = kern["decode"]["avg_us"] * 1e-6 * kern["decode"]["launches"]
         return {"elapsed": elapsed, "kv_bytes": kv_bytes, "kern": kern,
-                "gbs": kv_bytes / elapsed / 1e9, "achieved": kv_bytes / dec_s / 1e9}
+                "gbs": kv_bytes / elapsed / 1e9, "achieved": kv_bytes / dec_s / 1e9,
+                "step_ms_pct": pct(step_ms), "decode_us_pct": pct(dec_us)}
 
     r = run(0)
     res = dict(r, wl=wl, pool=pool, seqs=seqs,
@@ -375,30 +389,60 @@ def bench_forked(args, synth, pkv, shared):
     return res
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(args, wl, oracle):
-    """Time the oracle on the first sequences of the same workload (decode
-    step 0: every cached row plus the new one), within a wall budget."""
+    """Time the oracle on a sample of the same workload (decode step 0 of the
+    first sequences: every cached row plus the new one): once on one thread,
+    then the same sample split over every host core available to this process
+    (one oracle call per sequence per thread; the C oracle runs without the
+    interpreter lock).  The sample is the first sequences up to ~700K keys."""
+    from concurrent.futures import ThreadPoolExecutor
     q_all, k_all, v_all = wl.step(0)
-    spent, n, kvb = 0.0, 0, 0
     H, G, D = wl.n_heads, wl.n_kv_heads, wl.head_dim
+    sample, keys = [], 0
     for r in range(wl.M):
         kh, vh = wl.history(r)
-        K = np.concatenate([kh, k_all[r:r + 1]])
-        V = np.concatenate([vh, v_all[r:r + 1]])
-        t0 = time.perf_counter()
-        rc, _ = oracle.attn_contig(q_all[r:r + 1], K, V, H, G, D, True, wl.scale)
-        spent += time.perf_counter() - t0
-        assert rc == 0
-        n += 1
-        kvb += K.shape[0] * wl.kv_dim * 2 * 4
-        if spent > args.cpu_seconds:
+        sample.append((r, np.concatenate([kh, k_all[r:r + 1]]),
+                       np.concatenate([vh, v_all[r:r + 1]])))
+        keys += sample[-1][1].shape[0]
+        if keys >= args.cpu_keys:
             break
-    log("cpu oracle: %d sequences in %.2fs" % (n, spent))
+    kvb = keys * wl.kv_dim * 2 * 4
+
+    def one(item):
+        r, K, V = item
+        rc, _ = oracle.attn_contig(q_all[r:r + 1], K, V, H, G, D, True, wl.scale)
+        assert rc == 0
+
+    t0 = time.perf_counter()
+    for item in sample:
+        one(item)
+    t1 = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(one, sample))
+    tn = time.perf_counter() - t0
+    log("cpu oracle: %d sequences (%d keys): %.2fs on one thread, %.2fs on %d threads"
+        % (len(sample), keys, t1, tn, cores))
     return {
-        "value": kvb / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": "decode step of sequences 0..%d of %d (%d keys, one thread)"
-                  % (n - 1, wl.M, kvb // (wl.kv_dim * 8)),
-        "seq_tokens_per_s": n / spent,
+        "value": kvb / tn / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+        "sample": "decode step of sequences 0..%d of %d (%d keys), one oracle call per "
+                  "sequence per thread" % (len(sample) - 1, wl.M, keys),
+        "seq_tokens_per_s": len(sample) / tn,
+        "one_thread": {"value": kvb / t1 / 1e9, "unit": "GB/s", "cores": 1,
+                       "seq_tokens_per_s": len(sample) / t1},
+        "cpu_model": cpu_model(),
     }
 
 
@@ -511,6 +555,8 @@ def main():
         "pct_hbm_peak": 100.0 * d["gbs"] / HBM_PEAK_GBS,
         "kv_bytes_per_step": d["kv_bytes"] / args.steps,
         "kernels_us": {k: v["avg_us"] for k, v in d["kern"].items()},
+        "step_ms_percentiles": d["step_ms_pct"],
+        "decode_kernel_us_percentiles": d["decode_us_pct"],
         "rope": d["rope"],
         "verify": d.get("verify"),
         "roofline": {

@@ -430,6 +430,12 @@ int32_t pkv_profile_enable(pkv_pool *pool, int32_t on);
 int32_t pkv_profile_read(pkv_pool *pool, int32_t kernel, double *total_ms,
                          int64_t *launches);
 
+/* Wait for the recorded events and copy the duration (ms) of each of the
+ * first cap launches of one kernel id, in launch order; returns the number
+ * of launches recorded (which may exceed cap) or a negated code. */
+int32_t pkv_profile_samples(pkv_pool *pool, int32_t kernel, float *out_ms,
+                            int32_t cap);
+
 #ifdef __cplusplus
 }
 #endif

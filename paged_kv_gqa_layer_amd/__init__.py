@@ -287,6 +287,17 @@ class Pool:
     def profile_enable(self, on=True):
         return _check(lib().pkv_profile_enable(self._h, int(on)), "profile_enable")
 
+    def profile_samples(self, kernel):
+        """Per-launch durations (ms) of one kernel id since profiling was enabled."""
+        n = lib().pkv_profile_samples(self._h, kernel, None, 0)
+        if n < 0:
+            raise PKVError(-n, "profile_samples")
+        out = np.zeros(max(n, 1), np.float32)
+        n = lib().pkv_profile_samples(self._h, kernel, _vp(out), n)
+        if n < 0:
+            raise PKVError(-n, "profile_samples")
+        return out[:n].astype(np.float64)
+
     def profile_read(self, kernel):
         ms = C.c_double(0.0)
         n = C.c_int64(0)

@@ -1180,4 +1180,18 @@ int32_t pkv_profile_read(pkv_pool* pool, int32_t kernel, double* total_ms,
   return PKV_OK;
 }
 
+int32_t pkv_profile_samples(pkv_pool* pool, int32_t kernel, float* out_ms,
+                            int32_t cap) {
+  if (!pool || kernel < 0 || kernel >= PKV_K_COUNT || (cap > 0 && !out_ms))
+    return -PKV_ERR_BAD_ARG;
+  const auto& ev = pool->dev.prof_ev[kernel];
+  const int32_t n = static_cast<int32_t>(ev.size());
+  for (int32_t i = 0; i < n && i < cap; ++i) {
+    if (hipEventSynchronize(ev[i].second) != hipSuccess) return -PKV_ERR_DEVICE;
+    if (hipEventElapsedTime(&out_ms[i], ev[i].first, ev[i].second) != hipSuccess)
+      return -PKV_ERR_DEVICE;
+  }
+  return n;
+}
+
 }  // extern "C"
