@@ -576,9 +576,15 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   hipError_t e;
   if (uses_splits(kind, head_dim, group, block_size, n_q)) {
     if (pl.n_pre_items > 0) {
+      // shared prefixes: the prefix work and the own-key splits in one launch
       if constexpr (std::is_same<Map, PagedMap>::value) {
-        DeviceCtx::ProfScope ps(&dev, PKV_K_PREFIX, st);
-        if (pkv::launch_prefix_mfma(map, a, group, st) != hipSuccess) return PKV_ERR_DEVICE;
+        {
+          DeviceCtx::ProfScope ps(&dev, PKV_K_PREFIX, st);
+          if (pkv::launch_shared_decode(map, a, group, st) != hipSuccess)
+            return PKV_ERR_DEVICE;
+        }
+        DeviceCtx::ProfScope ps(&dev, PKV_K_MERGE, st);
+        return dev_status(pkv::launch_merge(a, st));
       }
     }
     {

@@ -169,10 +169,12 @@ hipError_t launch_verify_mfma(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
 hipError_t launch_verify_mfma(const ContigMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
-// Shared-prefix decode: every group's prefix keys once per kv head for all
-// its members' queries, into the members' prefix partial slots.
-hipError_t launch_prefix_mfma(const PagedMap& m, const AttnArgs& a,
-                              int32_t group, hipStream_t st);
+// Shared-prefix decode in one launch (group 1, 2, 4 or 8; decode_fast
+// shapes): every group's prefix keys once per kv head for all its members'
+// queries, into the members' prefix partial slots, and the rows' own-key
+// splits into theirs.
+hipError_t launch_shared_decode(const PagedMap& m, const AttnArgs& a,
+                                int32_t group, hipStream_t st);
 // Merges the key splits of every row with more than one (after decode_fast
 // or verify_mfma).
 hipError_t launch_merge(const AttnArgs& a, hipStream_t st);

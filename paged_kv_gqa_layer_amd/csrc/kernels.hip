@@ -266,20 +266,20 @@ __device__ __forceinline__ void merge_head(const AttnArgs& a, int32_t row,
                              2 * lane) = make_float2(o0 / L, o1 / L);
 }
 
+// One wave's work: work item item_idx (a (row, split) pair), kv head kvh;
+// lane = this thread's lane in its wave.
 template <int GROUP, class Map>
-__global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
+__device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
+                                            int32_t item_idx, int32_t kvh,
+                                            int lane) {
   constexpr int D = 128;
   constexpr int B = 16;
   constexpr int NI = B / 4;
-  const int32_t G = a.n_kv_heads;
-  const int32_t item_idx = blockIdx.x / G;
-  const int32_t kvh = blockIdx.x - item_idx * G;
   const int2 item = a.items[item_idx];
   const int32_t row = item.x, split = item.y;
   const RowDesc rd = a.rows[row];
   const int32_t nsp = rd.n_pre + rd.n_splits;  // partial results of the row
   const int32_t slot = rd.part_base + split;
-  const int lane = threadIdx.x;
   const int rr = lane >> 4;
   const int c = lane & 15;
 
@@ -492,6 +492,12 @@ __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
       }
     }
   }
+}
+
+template <int GROUP, class Map>
+__global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
+  const int32_t item_idx = blockIdx.x / a.n_kv_heads;
+  decode_wave<GROUP>(m, a, item_idx, blockIdx.x - item_idx * a.n_kv_heads, threadIdx.x);
 }
 
 // Split merge kernel: one wave per (row, query, query head) of a row with
@@ -976,19 +982,27 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // first member's page table; nothing is masked (every prefix key precedes
 // each member's new row) and each row's unnormalised state goes to its
 // prefix partial slot for merge_kernel.
+constexpr int kPfKT = 32;     // keys per tile
+constexpr int kPfKSTR = 132;  // padded LDS row strides (bank spread)
+constexpr int kPfVSTR = 136;
+// two K/V tile buffers: tile t+1 is stored while tile t is read
+struct PrefillLds {
+  float Ks2[2][kPfKT * kPfKSTR];
+  float Vs2[2][kPfKT * kPfVSTR];
+};
+
+// One workgroup's work (all 256 threads), workgroup number bid.
 template <int GROUP, bool PREFIX, class Map>
-// Two waves per SIMD (two workgroups per CU): the register budget is capped at
-// 256 so one workgroup's MFMAs overlap the other's softmax, LDS and barriers.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
+__device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
+                                              int32_t n_qt, int32_t n_wg,
+                                              int32_t bid, PrefillLds& sh) {
   constexpr int D = 128;
   constexpr int QPW = 32 / GROUP;  // queries per wave
-  constexpr int KT = 32;
-  constexpr int KSTR = 132;  // padded LDS row strides (bank spread)
-  constexpr int VSTR = 136;
-  // two K/V tile buffers: tile t+1 is stored while tile t is read
-  __shared__ float Ks2[2][KT * KSTR];
-  __shared__ float Vs2[2][KT * VSTR];
+  constexpr int KT = kPfKT;
+  constexpr int KSTR = kPfKSTR;
+  constexpr int VSTR = kPfVSTR;
+  auto& Ks2 = sh.Ks2;
+  auto& Vs2 = sh.Vs2;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -1008,7 +1022,7 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
   int64_t slot = 0;  // PREFIX: the row's partial slot
   if constexpr (!PREFIX) {
     // Keep all query tiles of one (row, kv head) on one XCD (they share K/V).
-    const int32_t b = blockIdx.x;
+    const int32_t b = bid;
     const int32_t Lw = (n_wg % 8 == 0) ? (b % 8) * (n_wg / 8) + b / 8 : b;
     const int32_t row = Lw / (G * n_qt);
     const int32_t rem = Lw - row * G * n_qt;
@@ -1030,8 +1044,8 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
     const int32_t wq_last = min(q0 + QPW * w + QPW - 1, n_q - 1);
     w_lim = (wq_first > wq_last) ? 0 : (a.causal ? total_k - n_q + wq_last + 1 : total_k);
   } else {
-    const int32_t item = blockIdx.x / G;
-    kvh = blockIdx.x - item * G;
+    const int32_t item = bid / G;
+    kvh = bid - item * G;
     const int4 it = reinterpret_cast<const int4*>(a.pre_items)[item];
     const int4 gd = reinterpret_cast<const int4*>(a.groups)[it.x];
     k_first = it.y * kPrefixSplit;
@@ -1207,6 +1221,35 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
   }
 }
 
+// Two waves per SIMD (two workgroups per CU): the register budget is capped at
+// 256 so one workgroup's MFMAs overlap the other's softmax, LDS and barriers.
+template <int GROUP, class Map>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
+  __shared__ PrefillLds sh;
+  prefill_block<GROUP, false>(m, a, n_qt, n_wg, blockIdx.x, sh);
+}
+
+// Shared-prefix decode in one launch: workgroups [0, n_pre_items * kv heads)
+// run the prefix items (prefix mode of the prefill work), the rest run four
+// decode work items each, one per wave, over the rows' own keys.  The two
+// kinds write disjoint partial slots; the decode waves use no LDS and no
+// barrier, so they fill the CUs beside the longer prefix workgroups.
+template <int GROUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void shared_decode_kernel(PagedMap m, AttnArgs a) {
+  __shared__ PrefillLds sh;
+  const int32_t n_pre_wg = a.n_pre_items * a.n_kv_heads;
+  if (static_cast<int32_t>(blockIdx.x) < n_pre_wg) {
+    prefill_block<GROUP, true>(m, a, 0, 0, blockIdx.x, sh);
+    return;
+  }
+  const int32_t wv = (blockIdx.x - n_pre_wg) * 4 + (threadIdx.x >> 6);
+  if (wv >= a.n_items * a.n_kv_heads) return;
+  const int32_t item_idx = wv / a.n_kv_heads;
+  decode_wave<GROUP>(m, a, item_idx, wv - item_idx * a.n_kv_heads, threadIdx.x & 63);
+}
+
 template <class Map, bool ONE>
 hipError_t append_impl(const Map& m, const RowDesc* rows, const float* K,
                        const float* V, int32_t M, int32_t n, int32_t kv_dim,
@@ -1263,16 +1306,15 @@ hipError_t verify_impl(const Map& m, const AttnArgs& a, int32_t group,
   return hipGetLastError();
 }
 
-template <class Map>
-hipError_t prefix_impl(const Map& m, const AttnArgs& a, int32_t group,
-                       hipStream_t st) {
-  if (a.n_pre_items <= 0) return hipSuccess;
-  const dim3 grid(a.n_pre_items * a.n_kv_heads);
+hipError_t shared_decode_impl(const PagedMap& m, const AttnArgs& a, int32_t group,
+                              hipStream_t st) {
+  const int64_t waves = (int64_t)a.n_items * a.n_kv_heads;
+  const dim3 grid(a.n_pre_items * a.n_kv_heads + (waves + 3) / 4);
   switch (group) {
-    case 1: prefill_mfma_kernel<1, true, Map><<<grid, 256, 0, st>>>(m, a, 0, 0); break;
-    case 2: prefill_mfma_kernel<2, true, Map><<<grid, 256, 0, st>>>(m, a, 0, 0); break;
-    case 4: prefill_mfma_kernel<4, true, Map><<<grid, 256, 0, st>>>(m, a, 0, 0); break;
-    case 8: prefill_mfma_kernel<8, true, Map><<<grid, 256, 0, st>>>(m, a, 0, 0); break;
+    case 1: shared_decode_kernel<1><<<grid, 256, 0, st>>>(m, a); break;
+    case 2: shared_decode_kernel<2><<<grid, 256, 0, st>>>(m, a); break;
+    case 4: shared_decode_kernel<4><<<grid, 256, 0, st>>>(m, a); break;
+    case 8: shared_decode_kernel<8><<<grid, 256, 0, st>>>(m, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1298,7 +1340,7 @@ hipError_t prefill_group(const Map& m, const AttnArgs& a, hipStream_t st) {
   constexpr int32_t qt = prefill_q_tile(GROUP);
   const int32_t n_qt = (a.n_q + qt - 1) / qt;
   const int32_t n_wg = a.n_rows * a.n_kv_heads * n_qt;
-  prefill_mfma_kernel<GROUP, false, Map><<<n_wg, 256, 0, st>>>(m, a, n_qt, n_wg);
+  prefill_mfma_kernel<GROUP, Map><<<n_wg, 256, 0, st>>>(m, a, n_qt, n_wg);
   return hipGetLastError();
 }
 
@@ -1375,9 +1417,9 @@ hipError_t launch_verify_mfma(const ContigMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st) {
   return verify_impl(m, a, group, st);
 }
-hipError_t launch_prefix_mfma(const PagedMap& m, const AttnArgs& a,
-                              int32_t group, hipStream_t st) {
-  return prefix_impl(m, a, group, st);
+hipError_t launch_shared_decode(const PagedMap& m, const AttnArgs& a,
+                                int32_t group, hipStream_t st) {
+  return shared_decode_impl(m, a, group, st);
 }
 hipError_t launch_merge(const AttnArgs& a, hipStream_t st) {
   return merge_impl(a, st);
