@@ -207,6 +207,7 @@ struct RowPlan {
   int32_t n_items = 0;      // split decode items (the rows' own key splits)
   int32_t n_slots = 0;      // partial-result slots (own splits + prefix splits)
   int32_t max_parts = 0;    // most partial results of one row
+  int32_t split_keys = 0;   // key positions per own-key split
   size_t item_off = 0;      // int32 offset of the (row, split) item list
   // shared-prefix decode (empty otherwise): int32 offsets in the blob
   int32_t n_pre_items = 0;
@@ -223,11 +224,14 @@ struct RowIn {
 // Row blob: RowDesc[M], then the split items as (row, split) pairs -- every
 // full split row by row, then the partial last splits longest first.  The
 // split plan is for n_q new rows per sequence (total_k = start + n_q): the
-// row's own keys [k_off, total_k) are cut into split_keys(n_q)-key splits.
+// row's own keys [k_off, total_k) are cut into split_keys(n_q, shared)-key
+// splits (shared: a shared-prefix decode plan).
 template <class F>
-RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, F rowinfo) {
+RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, bool shared,
+                   F rowinfo) {
   RowPlan pl;
-  const int32_t split = pkv::split_keys(n_q);
+  const int32_t split = pkv::split_keys(n_q, shared);
+  pl.split_keys = split;
   v.assign(static_cast<size_t>(M) * pkv::kRowInts, 0);
   std::vector<std::pair<int32_t, int32_t>> tails;  // (partial keys, row)
   pl.item_off = v.size();
@@ -440,7 +444,8 @@ hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
     const bool shared = shared_heads > 0;
     if (shared) find_shared(p->meta, seqs, M, shared_heads, &p->shared);
     const int32_t B = p->meta.block_size();
-    p->plan = build_rows(p->rows, M, n, [&](int32_t r) {
+    const bool grouped = shared && !p->shared.groups.empty();
+    p->plan = build_rows(p->rows, M, n, grouped, [&](int32_t r) {
       const pkv::SeqMeta* q = p->meta.seq(seqs[r]);
       RowIn in;
       in.start = q->seq_len;
@@ -568,7 +573,7 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   a.qscale = static_cast<float>(static_cast<double>(scale) * kLog2e);
   a.n_items = pl.n_items;
   a.rope = rope;
-  a.split_keys = pkv::split_keys(n_q);
+  a.split_keys = pl.split_keys;
   a.pre_items = rows_dev + pl.pre_off;
   a.groups = rows_dev + pl.group_off;
   a.members = rows_dev + pl.member_off;
@@ -859,7 +864,7 @@ size_t pool_workspace_bytes(pkv_pool* pool, const int32_t* seqs, int32_t M,
   SharedPlan sp;
   if (sh > 0) find_shared(m, seqs, M, sh, &sp);
   std::vector<int32_t> tmp;
-  const RowPlan pl = build_rows(tmp, M, n_q, [&](int32_t r) {
+  const RowPlan pl = build_rows(tmp, M, n_q, sh > 0 && !sp.groups.empty(), [&](int32_t r) {
     RowIn in;
     in.start = m.seq(seqs[r])->seq_len;
     if (sh > 0) {
@@ -991,7 +996,7 @@ int32_t contig_rows(const pkv_contig* c, const int32_t* slots,
     if (c->rope && static_cast<int64_t>(seq_lens[r]) + n > c->rope->max_positions)
       return PKV_ERR_CAPACITY;
   }
-  *pl = build_rows(rows, M, n, [&](int32_t r) {
+  *pl = build_rows(rows, M, n, false, [&](int32_t r) {
     RowIn in;
     in.start = seq_lens[r];
     in.pt_off = slots[r];
@@ -1039,7 +1044,7 @@ size_t contig_workspace_bytes(const int32_t* seq_lens, int32_t M, int32_t n_q,
     if (seq_lens[r] < 0) return static_cast<size_t>(-1);
   if (!uses_splits(kind, head_dim, n_heads / n_kv_heads, block_size, n_q)) return 0;
   std::vector<int32_t> tmp;
-  const RowPlan pl = build_rows(tmp, M, n_q, [&](int32_t r) {
+  const RowPlan pl = build_rows(tmp, M, n_q, false, [&](int32_t r) {
     RowIn in;
     in.start = seq_lens[r];
     return in;

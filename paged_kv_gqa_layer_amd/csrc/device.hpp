@@ -73,10 +73,17 @@ struct ContigMap {
 // Key positions per split of the specialised decode kernel (a multiple of
 // its 16-row page).
 constexpr int32_t kDecodeSplit = 512;
+// Own keys per split in a shared-prefix decode plan: a forked row's own keys
+// follow its shared prefix, which the prefix workgroups cover beside them,
+// so shorter splits keep the own-key waves from outlasting the prefix work.
+constexpr int32_t kSharedOwnSplit = 128;
 // Key positions per split for n_q new rows per sequence: with more query
 // rows per kv head each key costs more work, so splits are longer and the
 // partial results fewer.
-inline int32_t split_keys(int32_t n_q) { return n_q <= 4 ? kDecodeSplit : 2 * kDecodeSplit; }
+inline int32_t split_keys(int32_t n_q, bool shared = false) {
+  if (shared) return kSharedOwnSplit;
+  return n_q <= 4 ? kDecodeSplit : 2 * kDecodeSplit;
+}
 // Queries per workgroup of the MFMA prefill kernel: 4 waves of 32 MFMA rows,
 // each row one (query, head of the group).
 constexpr int32_t prefill_q_tile(int32_t group) { return 128 / group; }
@@ -116,7 +123,7 @@ struct AttnArgs {
   // rotary table [positions][head_dim/2] of (cos, sin), or null: queries are
   // turned at their positions before the scores
   const double2* rope;
-  int32_t split_keys;  // key positions per split (split_keys(n_q))
+  int32_t split_keys;  // key positions per split (split_keys(n_q, shared))
   // shared-prefix decode: prefix work items (group, split, row block) and the
   // groups they refer to
   const int32_t* pre_items;  // [n_pre_items][4]

@@ -284,8 +284,8 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
   const int c = lane & 15;
 
   const int32_t total_k = rd.start + 1;
-  const int32_t k_begin = rd.k_off + split * kDecodeSplit;
-  const int32_t k_end = min(total_k, k_begin + kDecodeSplit);
+  const int32_t k_begin = rd.k_off + split * a.split_keys;
+  const int32_t k_end = min(total_k, k_begin + a.split_keys);
   const int32_t p_begin = k_begin / B;
   const int32_t p_end = (k_end + B - 1) / B;
 
@@ -1230,21 +1230,24 @@ void prefill_mfma_kernel(Map m, AttnArgs a, int32_t n_qt, int32_t n_wg) {
   prefill_block<GROUP, false>(m, a, n_qt, n_wg, blockIdx.x, sh);
 }
 
-// Shared-prefix decode in one launch: workgroups [0, n_pre_items * kv heads)
-// run the prefix items (prefix mode of the prefill work), the rest run four
-// decode work items each, one per wave, over the rows' own keys.  The two
-// kinds write disjoint partial slots; the decode waves use no LDS and no
-// barrier, so they fill the CUs beside the longer prefix workgroups.
+// Shared-prefix decode in one launch: the first workgroups run four decode
+// work items each, one per wave, over the rows' own keys; the last
+// n_pre_items * kv heads run the prefix items (prefix mode of the prefill
+// work).  The two kinds write disjoint partial slots.  The decode waves use
+// no LDS and no barrier; dispatched first, they take one workgroup slot of a
+// CU each, which leaves the prefix workgroups spread one per CU (measured
+// ~8% faster on the forked batch than prefix workgroups first).
 template <int GROUP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void shared_decode_kernel(PagedMap m, AttnArgs a) {
   __shared__ PrefillLds sh;
   const int32_t n_pre_wg = a.n_pre_items * a.n_kv_heads;
-  if (static_cast<int32_t>(blockIdx.x) < n_pre_wg) {
-    prefill_block<GROUP, true>(m, a, 0, 0, blockIdx.x, sh);
+  const int32_t n_dec_wg = gridDim.x - n_pre_wg;
+  if (static_cast<int32_t>(blockIdx.x) >= n_dec_wg) {
+    prefill_block<GROUP, true>(m, a, 0, 0, blockIdx.x - n_dec_wg, sh);
     return;
   }
-  const int32_t wv = (blockIdx.x - n_pre_wg) * 4 + (threadIdx.x >> 6);
+  const int32_t wv = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (wv >= a.n_items * a.n_kv_heads) return;
   const int32_t item_idx = wv / a.n_kv_heads;
   decode_wave<GROUP>(m, a, item_idx, wv - item_idx * a.n_kv_heads, threadIdx.x & 63);
