@@ -364,7 +364,7 @@ def bench_forked(args, synth, pkv, shared):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     kern = {}
-    for name, kid in (("append", pkv.K_APPEND), ("prefix", pkv.K_PREFIX),
+    for name, kid in (("append", pkv.K_APPEND), ("shared_decode", pkv.K_PREFIX),
                       ("decode", pkv.K_DECODE), ("merge", pkv.K_MERGE),
                       ("cow", pkv.K_COW)):
         ms, n = pool.profile_read(kid)
@@ -382,10 +382,11 @@ def bench_forked(args, synth, pkv, shared):
         "step": "ensure_append + append_layer + %s + advance"
                 % ("attn_paged_decode_shared" if shared else "attn_paged_decode"),
     }
-    log("forked%s: %.3f ms/step, logical %.0f GB/s, unique %.0f GB/s, prefix %.1f us, "
-        "decode %.1f us, merge %.1f us"
+    log("forked%s: %.3f ms/step, logical %.0f GB/s, unique %.0f GB/s, %s %.1f us, "
+        "merge %.1f us"
         % (" shared" if shared else "", res["ms_per_step"], res["logical_gbs"],
-           res["unique_gbs"], kern["prefix"], kern["decode"], kern["merge"]))
+           res["unique_gbs"], "shared_decode" if shared else "decode",
+           kern["shared_decode" if shared else "decode"], kern["merge"]))
     return res
 
 

@@ -261,7 +261,7 @@ size_t pkv_decode_shared_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
  * Rows of the batch whose page tables begin with the same full pages (at
  * least 16 of them) form a group; the group's common prefix is attended once
  * per kv head for all members' queries (MFMA), each row's remaining keys by
- * the decode kernel, and the partial results are merged.  Outputs agree with
+ * decode waves of the same launch, and the partial results are merged.  Outputs agree with
  * pkv_attn_paged_decode within the float tolerance, not bit for bit, and a
  * row's bits depend on the group it falls in (which other rows are in the
  * batch).  Needs head_dim 128 and 16-row pages with a decode group of 1, 2,
@@ -418,7 +418,8 @@ int32_t pkv_pool_free_stack(pkv_pool *pool, int64_t *out, int32_t cap);
 #define PKV_K_PREFILL 3
 #define PKV_K_COW 4
 #define PKV_K_VERIFY 5   /* the split multi-query kernel */
-#define PKV_K_PREFIX 6   /* the shared-prefix kernel */
+#define PKV_K_PREFIX 6   /* the shared-prefix decode kernel (prefix and own
+                            keys in one launch) */
 #define PKV_K_COUNT 7
 
 /* on != 0: record a HIP event pair on the launch stream around every kernel
