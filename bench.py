@@ -32,6 +32,7 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 VERIFY_NQ = (4, 8)       # drafted tokens verified per sequence and step
 VERIFY_ROWS_MAX = 8
+COLD_STEPS = 10  # decode steps each preceded by a cache-evicting 1 GiB write
 FP32_MFMA_PEAK_TFLOPS = 157.3
 METRIC = ("paged GQA decode: achieved KV HBM GB/s (% peak) + "
           "seq-tokens/s at M=256")
@@ -151,7 +152,8 @@ def bench_decode(args, synth, pkv):
     mk = synth.decode_m256 if args.workload == "decode_m256" else synth.decode_m32
     n_steps = args.warmup + args.steps
     # head-room for the plain run, the rotary run and the verify runs
-    wl = mk(max_steps=2 * n_steps + 1 + VERIFY_ROWS_MAX * (n_steps + 2) * len(VERIFY_NQ))
+    wl = mk(max_steps=2 * n_steps + COLD_STEPS + 1 +
+            VERIFY_ROWS_MAX * (n_steps + 2) * len(VERIFY_NQ))
     H, G, D = wl.n_heads, wl.n_kv_heads, wl.head_dim
     M = wl.M
     log("workload %s: M=%d, cached rows %d..%d (sum %d), pool %d blocks (%.2f GB)"
@@ -174,7 +176,8 @@ def bench_decode(args, synth, pkv):
     out = torch.empty((M, H * D), device="cuda")
     seqs_np = np.asarray(seqs, np.int32)
     # workspace for the longest step (contexts grow by one row per step)
-    wsb = int(sum(math.ceil((int(c) + 2 * n_steps + 1) / 512) for c in wl.ctx)) * H * (D + 2) * 4
+    wsb = int(sum(math.ceil((int(c) + 2 * n_steps + COLD_STEPS + 1) / 512)
+                  for c in wl.ctx)) * H * (D + 2) * 4
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     scale = wl.scale
 
@@ -241,6 +244,41 @@ def bench_decode(args, synth, pkv):
     log("decode + rope: %.3f ms/step, %.0f GB/s step, append %.1f us, decode %.1f us"
         % (1e3 * rr["elapsed"] / args.steps, rr["gbs"], rr["kern"]["append"]["avg_us"],
            rr["kern"]["decode"]["avg_us"]))
+
+    # Cache-cold steps: before each, a 1 GiB read evicts the L2s and the
+    # 256 MB Infinity Cache (clean lines, so the step pays no write-back of
+    # the eviction), and no step reads K/V left there by the previous one;
+    # only the step itself is inside the events.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush.sum()
+    t_first = 2 * n_steps
+    pool.profile_enable(True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(COLD_STEPS)]
+    cold_bytes = []
+    for i in range(COLD_STEPS):
+        flush.sum()
+        ev[i][0].record()
+        step(t_first + i)
+        ev[i][1].record()
+        cold_bytes.append(int((wl.ctx.astype(np.int64) + t_first + i + 1).sum())
+                          * 2 * wl.kv_dim * 4)
+    torch.cuda.synchronize()
+    cold_ms = [a.elapsed_time(b) for a, b in ev]
+    cold_dec = 1e3 * pool.profile_samples(pkv.K_DECODE)
+    pool.profile_enable(False)
+    del flush
+    res["cold"] = {
+        "steps": COLD_STEPS,
+        "step_ms_percentiles": pct(cold_ms),
+        "decode_kernel_us_percentiles": pct(cold_dec),
+        "kernel_gbs_median": float(np.median(np.asarray(cold_bytes) /
+                                             (np.asarray(cold_dec) * 1e-6) / 1e9)),
+        "note": "each step preceded by a 1 GiB device read (outside the events)",
+    }
+    log("decode, cache-cold: step p50 %.3f ms, kernel p50 %.1f us -> %.0f GB/s"
+        % (res["cold"]["step_ms_percentiles"]["p50"],
+           res["cold"]["decode_kernel_us_percentiles"]["p50"], res["cold"]["kernel_gbs_median"]))
     if not args.no_verify:
         res["verify"] = [bench_verify(args, wl, pool, seqs, n_q, pkv, torch)
                          for n_q in VERIFY_NQ]
@@ -559,6 +597,7 @@ def main():
         "step_ms_percentiles": d["step_ms_pct"],
         "decode_kernel_us_percentiles": d["decode_us_pct"],
         "rope": d["rope"],
+        "cold": d["cold"],
         "verify": d.get("verify"),
         "roofline": {
             "bound": "hbm", "achieved": d["achieved"], "peak": HBM_PEAK_GBS,
