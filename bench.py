@@ -485,6 +485,48 @@ def cpu_baseline(args, wl, oracle):
     }
 
 
+def cpu_baseline_prefill(synth, oracle, n_last=16):
+    """The oracle on a sample of the prefill workload: the last n_last chunk
+    queries of every sequence (each sees ~4K keys), one oracle call per
+    sequence; once on one thread, then over the host cores.  Reported in
+    TFLOP/s of the same algorithmic flops as the kernel (4 * D * H per
+    visible key)."""
+    from concurrent.futures import ThreadPoolExecutor
+    wl = synth.prefill_8x3584p512()
+    H, G, D = wl.n_heads, wl.n_kv_heads, wl.head_dim
+    sample = []
+    for r in range(wl.M):
+        kh, vh = wl.history(r)
+        q, k, v = wl.chunk_inputs(r)
+        sample.append((q[-n_last:], np.concatenate([kh, k]), np.concatenate([vh, v])))
+    total_k = wl.cached + wl.chunk
+    flops = wl.M * sum(4 * D * H * (total_k - n_last + i + 1) for i in range(n_last))
+
+    def one(item):
+        q, K, V = item
+        rc, _ = oracle.attn_contig(q, K, V, H, G, D, True, wl.scale)
+        assert rc == 0
+
+    t0 = time.perf_counter()
+    for item in sample:
+        one(item)
+    t1 = time.perf_counter() - t0
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(one, sample))
+    tn = time.perf_counter() - t0
+    log("cpu oracle, prefill: %d queries: %.2fs on one thread, %.2fs on %d threads"
+        % (wl.M * n_last, t1, tn, min(cores, wl.M)))
+    return {
+        "value": flops / tn / 1e12, "unit": "TFLOP/s", "cores": min(cores, wl.M),
+        "kind": "oracle",
+        "sample": "last %d chunk queries of each of the %d sequences (%.2e flop), one "
+                  "oracle call per sequence per thread" % (n_last, wl.M, flops),
+        "one_thread": {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "cores": 1},
+    }
+
+
 def bench_prefill(args, synth, pkv):
     import torch
     wl = synth.prefill_8x3584p512()
@@ -618,6 +660,8 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         line["cpu_baseline"] = cpu_baseline(args, wl, oracle)
+        if not args.no_prefill:
+            line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(synth, oracle)
     print(json.dumps(line), flush=True)
 
 
