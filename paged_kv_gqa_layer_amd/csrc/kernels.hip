@@ -1027,7 +1027,9 @@ __device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
     const int32_t row = Lw / (G * n_qt);
     const int32_t rem = Lw - row * G * n_qt;
     kvh = rem / n_qt;
-    const int32_t qt = rem - kvh * n_qt;
+    // longest query tiles (most visible keys) first: the short ones fill the
+    // slots that free up last
+    const int32_t qt = n_qt - 1 - (rem - kvh * n_qt);
     rd = a.rows[row];
     const int32_t n_q = a.n_q;
     const int32_t total_k = rd.start + n_q;
