@@ -20,4 +20,7 @@ def test_readme_example_runs():
     pool, seqs, out = ns["pool"], ns["seqs"], ns["out"]
     assert all(pool.seq_len(int(s)) == 1 for s in seqs)
     assert pool.seq_len(ns["child"]) == 0
-    assert bool(torch.isfinite(out).all())
+    # one visible key per sequence: every head's output is its kv head's V row
+    v = ns["v"]
+    expect = v.view(4, 8, 1, 128).expand(4, 8, 4, 128).reshape(4, 32 * 128)
+    assert torch.equal(out, expect)
