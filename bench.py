@@ -130,19 +130,29 @@ class HistoryFiller:
         self.ex.shutdown()
 
 
+def kernel_code_digest(path):
+    """SHA-256 of a kernel source with its comments and blank space removed, so
+    that the digest changes with the code and not with its comments."""
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def traffic_for(kernel_name, algorithmic_bytes_per_launch):
     """HBM bytes per launch implied by the committed rocprofv3 counter summary
     (its calibrated FETCH_SIZE + WRITE_SIZE over the algorithmic bytes of the
     profiled launches, times this run's algorithmic bytes per launch), if it
-    was taken on the current kernel source; else None."""
+    was taken on the current kernel code (comments aside); else None."""
     path = os.path.join(ROOT, "profiles", "%s_traffic.json" % kernel_name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
     src = os.path.join(ROOT, "paged_kv_gqa_layer_amd", "csrc", "kernels.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if t.get("kernels_hip_sha256") != sha:
+    if t.get("kernels_hip_code_sha256") != kernel_code_digest(src):
         return None
     return t["traffic_over_algorithmic"] * algorithmic_bytes_per_launch
 

@@ -519,7 +519,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------------------
 // Multi-row MFMA attention engine (FP32 MFMA 16x16x4, head_dim 128, 16-row
-// pages), used by the multi-query decode and the shared-prefix kernels.  A
+// pages), used by the multi-query decode kernel.  A
 // workgroup of NB waves runs 16 NB query rows of one kv head over one key
 // range; each wave owns 16 rows (lane l: row l%16).
 //
