@@ -580,6 +580,8 @@ def bench_prefill(args, synth, pkv):
     pool.profile_enable(False)
     visible = M * sum(wl.cached + i + 1 for i in range(wl.chunk))
     flops = 4 * D * H * visible
+    # bytes the launch must move: Q read and out written, K/V of every row read
+    unique_bytes = (2 * M * wl.chunk * H * D + M * (wl.cached + wl.chunk) * 2 * G * D) * 4
     kern_s = ms * 1e-3 / n
     tf = flops / kern_s / 1e12
     log("prefill: step %.3f ms, kernel %.3f ms -> %.1f TFLOP/s (%.1f%% of FP32 MFMA peak)"
@@ -593,7 +595,8 @@ def bench_prefill(args, synth, pkv):
         "kernel_ms": 1e3 * kern_s, "flops_per_step": flops,
         "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tf / FP32_MFMA_PEAK_TFLOPS,
-                     "traffic": None},
+                     "traffic": traffic_for("prefill_mfma_kernel", unique_bytes),
+                     "unique_bytes_per_launch": unique_bytes},
     }
 
 
