@@ -169,3 +169,65 @@ def test_large_batch_of_short_contexts():
                    ws=cws)
     torch.cuda.synchronize()
     assert bits_equal(out, cout)
+
+
+def test_group_16_generic_path_and_unsupported_shapes():
+    """Group 16 (beyond the fast kernels' 1/2/4/8) runs the generic kernel for
+    decode and prefill and matches the oracle; group 17, or a group whose q
+    and o vectors do not fit the generic kernel's LDS, is refused with
+    UNSUPPORTED and leaves the output untouched."""
+    rng = np.random.default_rng(16)
+    Gk, Dk, Bk = 1, 64, 16
+    pool = pkv.Pool(64, Bk, 1, Gk, Dk, max_seqs=4)
+    pool.set_free_order(rng.permutation(pool.n_blocks))
+    seqs = [pool.seq_new(300), pool.seq_new(300)]
+    hist = [(_rand(rng, (n, Gk * Dk)), _rand(rng, (n, Gk * Dk))) for n in (131, 40)]
+    fill_history(pool, seqs, lambda r: hist[r])
+    scale = float(np.float32(1 / math.sqrt(Dk)))
+    for n_q, Hk in ((1, 16), (5, 16)):
+        Q = _rand(rng, (2 * n_q, Hk * Dk))
+        K = _rand(rng, (2 * n_q, Gk * Dk))
+        V = _rand(rng, (2 * n_q, Gk * Dk))
+        pool.ensure_append(seqs, n_q, check=True)
+        pool.append_layer(seqs, n_q, 0, dev(K), dev(V), check=True)
+        out = torch.full((2 * n_q, Hk * Dk), float("nan"), device="cuda")
+        if n_q == 1:
+            pool.attn_paged_decode(seqs, 0, Hk, Gk, Dk, dev(Q), scale, out, check=True)
+        else:
+            pool.attn_paged_prefill(seqs, n_q, 0, Hk, Gk, Dk, dev(Q), True, scale, out,
+                                    check=True)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for r in range(2):
+            rows = slice(r * n_q, (r + 1) * n_q)
+            kk = np.concatenate([hist[r][0], K[rows]])
+            vv = np.concatenate([hist[r][1], V[rows]])
+            rc, ref = oracle.attn_contig(Q[rows], kk, vv, Hk, Gk, Dk, True, scale)
+            assert rc == 0
+            assert_close(got[rows], ref, "group 16 n_q %d row %d" % (n_q, r))
+        pool.advance(seqs, n_q, check=True)
+        hist = [(np.concatenate([hist[r][0], K[r * n_q:(r + 1) * n_q]]),
+                 np.concatenate([hist[r][1], V[r * n_q:(r + 1) * n_q]])) for r in range(2)]
+    # group 17
+    pool.ensure_append(seqs, 1, check=True)
+    pool.append_layer(seqs, 1, 0, dev(_rand(rng, (2, Dk))), dev(_rand(rng, (2, Dk))),
+                      check=True)
+    out = torch.full((2, 17 * Dk), 7.0, device="cuda")
+    q = dev(_rand(rng, (2, 17 * Dk)))
+    assert pool.attn_paged_decode(seqs, 0, 17, Gk, Dk, q, scale, out) == pkv.UNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    pool.close()
+    # group 16 at head_dim 600: q and o of the group exceed the generic LDS budget
+    Dl = 600
+    big = pkv.Pool(8, Bk, 1, Gk, Dl, max_seqs=2)
+    s = big.seq_new(32)
+    big.ensure_append([s], 1, check=True)
+    big.append_layer([s], 1, 0, dev(_rand(rng, (1, Dl))), dev(_rand(rng, (1, Dl))),
+                     check=True)
+    out = torch.full((1, 16 * Dl), 7.0, device="cuda")
+    q = dev(_rand(rng, (1, 16 * Dl)))
+    assert big.attn_paged_decode([s], 0, 16, Gk, Dl, q, 0.04, out) == pkv.UNSUPPORTED
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())
+    big.close()
