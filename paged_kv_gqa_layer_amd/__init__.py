@@ -67,6 +67,20 @@ def _dptr(t, what, numel=None):
     return C.c_void_p(t.data_ptr())
 
 
+def _ws(ws):
+    """(pointer, bytes) of a workspace: a contiguous CUDA tensor, or None."""
+    if ws is None:
+        return None, 0
+    import torch
+    if not isinstance(ws, torch.Tensor):
+        raise TypeError("ws must be a torch tensor")
+    if not ws.is_cuda:
+        raise ValueError("ws must be on the GPU")
+    if not ws.is_contiguous():
+        raise ValueError("ws must be contiguous")
+    return C.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size()
+
+
 def _check(rc, what, check=True):
     if check and rc != OK:
         raise PKVError(rc, what)
@@ -210,8 +224,7 @@ class Pool:
         q_dim = n_heads * head_dim
         qp = _dptr(Q, "Q", a.size * q_dim)
         op = _dptr(out, "out", a.size * q_dim)
-        wp = None if ws is None else C.c_void_p(ws.data_ptr())
-        wb = 0 if ws is None else ws.numel() * ws.element_size()
+        wp, wb = _ws(ws)
         return _check(lib().pkv_attn_paged_decode(
             self._h, _vp(a), a.size, layer, n_heads, n_kv_heads, head_dim, qp,
             float(scale), op, wp, wb, _stream(stream)), "attn_paged_decode", check)
@@ -226,8 +239,7 @@ class Pool:
         q_dim = n_heads * head_dim
         qp = _dptr(Q, "Q", a.size * q_dim)
         op = _dptr(out, "out", a.size * q_dim)
-        wp = None if ws is None else C.c_void_p(ws.data_ptr())
-        wb = 0 if ws is None else ws.numel() * ws.element_size()
+        wp, wb = _ws(ws)
         return _check(lib().pkv_attn_paged_decode_shared(
             self._h, _vp(a), a.size, layer, n_heads, n_kv_heads, head_dim, qp,
             float(scale), op, wp, wb, _stream(stream)), "attn_paged_decode_shared",
@@ -243,8 +255,7 @@ class Pool:
         q_dim = n_heads * head_dim
         qp = _dptr(Q, "Q", a.size * n_q * q_dim)
         op = _dptr(out, "out", a.size * n_q * q_dim)
-        wp = None if ws is None else C.c_void_p(ws.data_ptr())
-        wb = 0 if ws is None else ws.numel() * ws.element_size()
+        wp, wb = _ws(ws)
         return _check(lib().pkv_attn_paged_verify(
             self._h, _vp(a), a.size, n_q, layer, n_heads, n_kv_heads, head_dim, qp,
             float(scale), op, wp, wb, _stream(stream)), "attn_paged_verify", check)
@@ -344,8 +355,7 @@ class ContigCache:
                     ws=None, stream=None, check=True):
         s, l = _ids(slots), _ids(seq_lens)
         q_dim = n_heads * self.head_dim
-        wp = None if ws is None else C.c_void_p(ws.data_ptr())
-        wb = 0 if ws is None else ws.numel() * ws.element_size()
+        wp, wb = _ws(ws)
         return _check(lib().pkv_attn_contig_decode(
             C.byref(self.desc), _vp(s), _vp(l), s.size, layer, n_heads,
             self.n_kv_heads, self.head_dim, _dptr(Q, "Q", s.size * q_dim),
@@ -361,8 +371,7 @@ class ContigCache:
                     ws=None, stream=None, check=True):
         s, l = _ids(slots), _ids(seq_lens)
         q_dim = n_heads * self.head_dim
-        wp = None if ws is None else C.c_void_p(ws.data_ptr())
-        wb = 0 if ws is None else ws.numel() * ws.element_size()
+        wp, wb = _ws(ws)
         return _check(lib().pkv_attn_contig_verify(
             C.byref(self.desc), _vp(s), _vp(l), s.size, n_q, layer, n_heads,
             self.n_kv_heads, self.head_dim, _dptr(Q, "Q", s.size * n_q * q_dim),

@@ -192,3 +192,18 @@ def test_rope_table_argument_checks():
     p = pkv.Pool(4, 4, 1, 1, 4, device=None)
     assert L.pkv_pool_set_rope(p._h, None) == pkv.OK
     assert L.pkv_pool_set_rope(None, None) == pkv.BAD_ARG
+
+
+def test_binding_rejects_host_and_malformed_buffers():
+    """Pointers handed to the library must be contiguous device buffers; the
+    binding refuses host tensors before any call (a host pointer in a kernel
+    would fault the GPU)."""
+    import torch
+    with pytest.raises(ValueError):
+        pkv._ws(torch.empty(16, dtype=torch.uint8))
+    with pytest.raises(TypeError):
+        pkv._ws(np.empty(16, np.uint8))
+    with pytest.raises(ValueError):
+        pkv._dptr(torch.empty(4, dtype=torch.float32), "Q")
+    assert pkv._ws(None) == (None, 0)
+    assert pkv._dptr(None, "Q") is None
