@@ -1018,6 +1018,7 @@ __device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
   // needs at all (w_lim).
   RowDesc rd;
   int32_t kvh, k_first, k_lim, q_row, q_pos, mask_pos, w_lim;
+  int32_t w_mask_min;  // smallest mask position of the wave's rows
   bool row_valid;
   int64_t slot = 0;  // PREFIX: the row's partial slot
   if constexpr (!PREFIX) {
@@ -1045,6 +1046,7 @@ __device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
     const int32_t wq_first = q0 + QPW * w;
     const int32_t wq_last = min(q0 + QPW * w + QPW - 1, n_q - 1);
     w_lim = (wq_first > wq_last) ? 0 : (a.causal ? total_k - n_q + wq_last + 1 : total_k);
+    w_mask_min = a.causal ? total_k - n_q + wq_first : INT32_MAX;
   } else {
     const int32_t item = bid / G;
     kvh = bid - item * G;
@@ -1061,6 +1063,7 @@ __device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
     q_row = mrow;
     q_pos = md.start;
     mask_pos = INT32_MAX;
+    w_mask_min = INT32_MAX;
     w_lim = (m0 + QPW * w < gd.z) ? k_lim : 0;
     slot = md.part_base - md.n_pre + it.y;
   }
@@ -1109,6 +1112,18 @@ __device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
     const int32_t pg = k0 / 16;
     const float* p0 = m.page(rd, pg, kvh);
     const float* p1 = (k0 + 16 < k_lim) ? m.page(rd, pg + 1, kvh) : p0;
+    if (k0 + KT <= k_lim) {
+      // whole tile present: plain loads
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int key = ld_key + 8 * u;
+        const float* base = (u < 2) ? p0 : p1;
+        const int off = (key & 15) * D + ld_c;
+        kr[u] = ld4(base + off);
+        vr[u] = ld4(base + m.v_off + off);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int key = ld_key + 8 * u;
@@ -1152,11 +1167,17 @@ __device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
       }
       // mask and row max: this lane holds row lr, keys k0 + 8*(r/4) + 4*h + r%4
       float mx = kNegInf;
+      if (k0 + KT <= k_lim && k0 + KT - 1 <= w_mask_min) {
+        // every key of the tile is visible to every row of the wave
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int32_t key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (!(key < k_lim && key <= mask_pos)) S[r] = kNegInf;
-        mx = fmaxf(mx, S[r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int32_t key = k0 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (!(key < k_lim && key <= mask_pos)) S[r] = kNegInf;
+          mx = fmaxf(mx, S[r]);
+        }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       // finite: every row sees key k_first (causal rows see key 0 onwards)
