@@ -185,7 +185,8 @@ def bench_decode(args, synth, pkv):
         steps.append(tuple(torch.from_numpy(x).cuda() for x in (q, k, v)))
     out = torch.empty((M, H * D), device="cuda")
     seqs_np = np.asarray(seqs, np.int32)
-    # workspace for the longest step (contexts grow by one row per step)
+    # workspace for the longest step (contexts grow by one row per step); an
+    # upper bound: the library never splits finer than 512 keys
     wsb = int(sum(math.ceil((int(c) + 2 * n_steps + COLD_STEPS + 1) / 512)
                   for c in wl.ctx)) * H * (D + 2) * 4
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
@@ -642,7 +643,8 @@ def main():
             "block_size": wl.block_size, "layers": 1,
             "context_rows": [int(wl.ctx.min()), int(wl.ctx.max())],
             "mean_total_k": float(wl.ctx.mean() + 1 + args.warmup + (args.steps - 1) / 2),
-            "split_keys": 512, "placement": "random permutation",
+            "split_keys": "512 / 1024 / 2048 for rows below 4096 / 8192 / above",
+            "placement": "random permutation",
             "step": "ensure_append + append_layer + attn_paged_decode + advance",
         },
         "seq_tokens_per_s": d["seq_tok_s"],

@@ -232,9 +232,11 @@ size_t pkv_decode_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
 /* Batched decode: one new query row per sequence, already appended with
  * pkv_append_layer and not yet advanced, so total_k = seq_len + 1 and every
  * key is visible.  Q_dev, out_dev: [M, n_heads * head_dim], row r for
- * seqs[r].  Long contexts are split into fixed 512-row key ranges whose
- * partial softmax states are merged in a fixed order, so each output depends
- * only on its own sequence (independent of M, batch order and placement).
+ * seqs[r].  Long contexts are split into key ranges whose size follows from
+ * the sequence's own length alone (512 rows below 4096 keys, 1024 below
+ * 8192, 2048 above) and whose partial softmax states are merged in a fixed
+ * order, so each output depends only on its own sequence (independent of M,
+ * batch order and placement).
  * ws_dev: >= pkv_decode_workspace_bytes bytes (may be NULL when that is 0).
  * Errors in the pages' order: BAD_DIM (M, n_heads, n_kv_heads, head_dim
  * <= 0, or head shape != the pool's), BAD_GQA, SEQ, then BAD_ARG (layer,
@@ -287,8 +289,9 @@ size_t pkv_verify_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
  * source": header, "truncate unref" as the speculative-decode rewind; the
  * result is the prefill's, "nx_f32_attn_paged.nx source" header comment).
  * Q_dev, out_dev: [M * n_q, n_heads * head_dim], row r * n_q + i.  Keys are
- * cut into fixed splits (512 rows for n_q <= 4, 1024 above), merged in a
- * fixed order, so each output depends only on its own sequence.  Split kernel when
+ * cut into splits sized from the sequence's own length (as in decode for
+ * n_q <= 4, twice that above), merged in a fixed order, so each output
+ * depends only on its own sequence.  Split kernel when
  * n_q * (n_heads / n_kv_heads) <= 32 with head_dim 128 and 16-row pages
  * (n_q == 1 runs pkv_attn_paged_decode's kernels, bit for bit); other shapes
  * run the prefill kernels and need no workspace.  ws_dev: >=

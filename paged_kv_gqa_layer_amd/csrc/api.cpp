@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <type_traits>
 #include <unordered_map>
@@ -207,7 +208,6 @@ struct RowPlan {
   int32_t n_items = 0;      // split decode items (the rows' own key splits)
   int32_t n_slots = 0;      // partial-result slots (own splits + prefix splits)
   int32_t max_parts = 0;    // most partial results of one row
-  int32_t split_keys = 0;   // key positions per own-key split
   size_t item_off = 0;      // int32 offset of the (row, split) item list
   // shared-prefix decode (empty otherwise): int32 offsets in the blob
   int32_t n_pre_items = 0;
@@ -221,23 +221,26 @@ struct RowIn {
   int32_t append_block = -1;  // paged: block of page start / block_size
 };
 
-// Row blob: RowDesc[M], then the split items as (row, split) pairs -- every
-// full split row by row, then the partial last splits longest first.  The
-// split plan is for n_q new rows per sequence (total_k = start + n_q): the
-// row's own keys [k_off, total_k) are cut into split_keys(n_q, shared)-key
-// splits (shared: a shared-prefix decode plan).
+// Row blob: RowDesc[M], then the split items as (row, split) pairs, longest
+// first (the hardware starts workgroups in grid order, so the short items
+// fill the slots that free up last): full splits of the longest split size,
+// row by row, then shorter sizes, with each partial last split placed before
+// the first size it is longer than.  The split plan is for n_q new rows per
+// sequence (total_k = start + n_q): the row's own keys [k_off, total_k) are
+// cut into split_keys(own, n_q, shared)-key splits (shared: a shared-prefix
+// decode plan).
 template <class F>
 RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, bool shared,
                    F rowinfo) {
   RowPlan pl;
-  const int32_t split = pkv::split_keys(n_q, shared);
-  pl.split_keys = split;
   v.assign(static_cast<size_t>(M) * pkv::kRowInts, 0);
   std::vector<std::pair<int32_t, int32_t>> tails;  // (partial keys, row)
+  std::vector<int32_t> sizes;                      // distinct split sizes
   pl.item_off = v.size();
   for (int32_t r = 0; r < M; ++r) {
     const RowIn in = rowinfo(r);
     const int64_t own = static_cast<int64_t>(in.start) + n_q - in.k_off;
+    const int32_t split = pkv::split_keys(own, n_q, shared);
     const int32_t nsp = ceil_div(own, split);
     const int32_t rem = static_cast<int32_t>(own % split);
     int32_t* d = v.data() + static_cast<size_t>(r) * pkv::kRowInts;
@@ -248,22 +251,39 @@ RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, bool shared,
     d[4] = in.k_off;
     d[5] = in.n_pre;
     d[6] = in.append_block;
-    for (int32_t sp = 0; sp < (rem ? nsp - 1 : nsp); ++sp) {
-      v.push_back(r);
-      v.push_back(sp);
-    }
+    d[7] = split;
     pl.n_items += nsp;
     pl.n_slots += in.n_pre + nsp;
     pl.max_parts = std::max(pl.max_parts, in.n_pre + nsp);
     if (rem) tails.emplace_back(rem, r);
+    if (std::find(sizes.begin(), sizes.end(), split) == sizes.end()) sizes.push_back(split);
   }
   std::stable_sort(tails.begin(), tails.end(),
                    [](const std::pair<int32_t, int32_t>& x,
                       const std::pair<int32_t, int32_t>& y) { return x.first > y.first; });
-  for (const auto& t : tails) {
-    v.push_back(t.second);
-    v.push_back(v[static_cast<size_t>(t.second) * pkv::kRowInts + 2] - 1);
+  std::sort(sizes.begin(), sizes.end(), std::greater<int32_t>());
+  size_t ti = 0;
+  auto emit_tails_above = [&](int32_t keys) {
+    for (; ti < tails.size() && tails[ti].first > keys; ++ti) {
+      const int32_t r = tails[ti].second;
+      v.push_back(r);
+      v.push_back(v[static_cast<size_t>(r) * pkv::kRowInts + 2] - 1);
+    }
+  };
+  for (const int32_t size : sizes) {
+    emit_tails_above(size);
+    for (int32_t r = 0; r < M; ++r) {
+      const int32_t* d = v.data() + static_cast<size_t>(r) * pkv::kRowInts;
+      if (d[7] != size) continue;
+      const int64_t own = static_cast<int64_t>(d[0]) + n_q - d[4];
+      const int32_t n_full = static_cast<int32_t>(own / size);
+      for (int32_t sp = 0; sp < n_full; ++sp) {
+        v.push_back(r);
+        v.push_back(sp);
+      }
+    }
   }
+  emit_tails_above(0);
   return pl;
 }
 
@@ -573,7 +593,6 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   a.qscale = static_cast<float>(static_cast<double>(scale) * kLog2e);
   a.n_items = pl.n_items;
   a.rope = rope;
-  a.split_keys = pl.split_keys;
   a.pre_items = rows_dev + pl.pre_off;
   a.groups = rows_dev + pl.group_off;
   a.members = rows_dev + pl.member_off;

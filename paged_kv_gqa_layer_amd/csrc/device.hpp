@@ -7,10 +7,9 @@
 // batch row (uploaded once per pool version and batch, so all layers of a
 // step share it).
 //
-// Decode work items: each row's keys are cut into fixed splits (512 keys for
-// up to four new rows per sequence, 1024 beyond).  The item list holds
-// (row, split) pairs: every row's full splits first, then the rows' partial
-// last splits, longest first, so the end of the grid is filled with the
+// Decode work items: each row's keys are cut into splits whose size follows
+// from the row's own key count (split_keys).  The item list holds (row,
+// split) pairs, longest first, so the end of the grid is filled with the
 // shortest work.
 #pragma once
 
@@ -31,7 +30,7 @@ struct RowDesc {
   int32_t n_pre;       // partial slots of the shared prefix, part_base - n_pre ..
   int32_t append_block;  // paged: block of page start / block_size (where a
                          // one-row append lands), -1 if not yet reserved
-  int32_t pad;
+  int32_t split;       // decode: own keys per split (split_keys)
 };
 constexpr int kRowInts = sizeof(RowDesc) / sizeof(int32_t);
 
@@ -70,19 +69,22 @@ struct ContigMap {
   }
 };
 
-// Key positions per split of the specialised decode kernel (a multiple of
-// its 16-row page).
+// Shortest key split of the decode kernels (a multiple of the 16-row page).
 constexpr int32_t kDecodeSplit = 512;
 // Own keys per split in a shared-prefix decode plan: a forked row's own keys
 // follow its shared prefix, which the prefix workgroups cover beside them,
 // so shorter splits keep the own-key waves from outlasting the prefix work.
 constexpr int32_t kSharedOwnSplit = 128;
-// Key positions per split for n_q new rows per sequence: with more query
-// rows per kv head each key costs more work, so splits are longer and the
-// partial results fewer.
-inline int32_t split_keys(int32_t n_q, bool shared = false) {
+// Own keys per split of one row, from the row's own key count alone (so a
+// row's result does not depend on the rest of the batch): 512 below 4096
+// keys, 1024 below 8192, 2048 above -- longer rows take longer splits, which
+// cuts the per-wave start-up, partial writes and merge reads -- doubled for
+// more than 4 queries per row (each key costs more work), and the shared
+// own-key split in a shared-prefix plan.
+inline int32_t split_keys(int64_t own, int32_t n_q, bool shared = false) {
   if (shared) return kSharedOwnSplit;
-  return n_q <= 4 ? kDecodeSplit : 2 * kDecodeSplit;
+  int32_t s = own >= 8192 ? 4 * kDecodeSplit : own >= 4096 ? 2 * kDecodeSplit : kDecodeSplit;
+  return n_q <= 4 ? s : 2 * s;
 }
 // Queries per workgroup of the MFMA prefill kernel: 4 waves of 32 MFMA rows,
 // each row one (query, head of the group).
@@ -123,7 +125,6 @@ struct AttnArgs {
   // rotary table [positions][head_dim/2] of (cos, sin), or null: queries are
   // turned at their positions before the scores
   const double2* rope;
-  int32_t split_keys;  // key positions per split (split_keys(n_q, shared))
   // shared-prefix decode: prefix work items (group, split, row block) and the
   // groups they refer to
   const int32_t* pre_items;  // [n_pre_items][4]

@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void cow_kernel(float* base,
 
 // ---------------------------------------------------------------------------
 // Decode, head_dim 128, 16-row pages: one 64-lane wave per
-// (work item = row x 512-key split, kv head).
+// (work item = row x key split, kv head).
 //
 // Lane layout: lane = 16 * rr + c.  For each page the wave reads the kv
 // head's 16 x 128 K tile and V tile once, four positions per load step:
@@ -284,8 +284,8 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
   const int c = lane & 15;
 
   const int32_t total_k = rd.start + 1;
-  const int32_t k_begin = rd.k_off + split * a.split_keys;
-  const int32_t k_end = min(total_k, k_begin + a.split_keys);
+  const int32_t k_begin = rd.k_off + split * rd.split;
+  const int32_t k_end = min(total_k, k_begin + rd.split);
   const int32_t p_begin = k_begin / B;
   const int32_t p_end = (k_end + B - 1) / B;
 
@@ -800,8 +800,8 @@ void verify_mfma_kernel(Map m, AttnArgs a, int32_t group) {
   const int mq = lane >> 4;
   const int32_t n_q = a.n_q;
   const int32_t total_k = rd.start + n_q;
-  const int32_t k_begin = rd.k_off + split * a.split_keys;
-  const int32_t k_end = min(total_k, k_begin + a.split_keys);
+  const int32_t k_begin = rd.k_off + split * rd.split;
+  const int32_t k_end = min(total_k, k_begin + rd.split);
 
   // This lane's query row; rows past n_q * group hold zeros, see every key
   // of the split and are not written.
