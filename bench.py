@@ -186,8 +186,8 @@ def bench_decode(args, synth, pkv):
     out = torch.empty((M, H * D), device="cuda")
     seqs_np = np.asarray(seqs, np.int32)
     # workspace for the longest step (contexts grow by one row per step); an
-    # upper bound: the library never splits finer than 512 keys
-    wsb = int(sum(math.ceil((int(c) + 2 * n_steps + COLD_STEPS + 1) / 512)
+    # upper bound for any split of at least 128 keys
+    wsb = int(sum(math.ceil((int(c) + 2 * n_steps + COLD_STEPS + 1) / 128)
                   for c in wl.ctx)) * H * (D + 2) * 4
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     scale = wl.scale
@@ -310,7 +310,7 @@ def bench_verify(args, wl, pool, seqs, n_q, pkv, torch):
     out = torch.empty_like(Q)
     seqs_np = np.asarray(seqs, np.int32)
     max_len = max(pool.seq_len(s) for s in seqs) + n_q * (n_steps + 1)
-    ws = torch.empty(M * math.ceil(max_len / 512) * n_q * H * (D + 2) * 4,
+    ws = torch.empty(M * math.ceil(max_len / 128) * n_q * H * (D + 2) * 4,
                      dtype=torch.uint8, device="cuda")
     accept = rng.integers(1, n_q + 1, size=(n_steps, M))
 
