@@ -162,7 +162,7 @@ def bench_decode(args, synth, pkv):
     mk = synth.decode_m256 if args.workload == "decode_m256" else synth.decode_m32
     n_steps = args.warmup + args.steps
     # head-room for the plain run, the rotary run and the verify runs
-    wl = mk(max_steps=2 * n_steps + COLD_STEPS + 1 +
+    wl = mk(max_steps=3 * n_steps + COLD_STEPS + 1 +
             VERIFY_ROWS_MAX * (n_steps + 2) * len(VERIFY_NQ))
     H, G, D = wl.n_heads, wl.n_kv_heads, wl.head_dim
     M = wl.M
@@ -187,7 +187,7 @@ def bench_decode(args, synth, pkv):
     seqs_np = np.asarray(seqs, np.int32)
     # workspace for the longest step (contexts grow by one row per step); an
     # upper bound for any split of at least 128 keys
-    wsb = int(sum(math.ceil((int(c) + 2 * n_steps + COLD_STEPS + 1) / 128)
+    wsb = int(sum(math.ceil((int(c) + 3 * n_steps + COLD_STEPS + 1) / 128)
                   for c in wl.ctx)) * H * (D + 2) * 4
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     scale = wl.scale
@@ -199,12 +199,14 @@ def bench_decode(args, synth, pkv):
         pool.attn_paged_decode(seqs_np, 0, H, G, D, q, scale, out, ws=ws, check=True)
         pool.advance(seqs_np, 1, check=True)
 
-    def run(t_first):
+    def run(t_first, kernels=None):
         """warmup + timed steps from step index t_first (rows cached before
-        step t: ctx + t)."""
+        step t: ctx + t); the library times the launches of `kernels` (ids,
+        None: all) with HIP events on its stream."""
         for t in range(t_first, t_first + args.warmup):
             step(t)
         torch.cuda.synchronize()
+        pool.profile_kernels(kernels)
         pool.profile_enable(True)
         # per-step GPU time: events on the stream the library is given
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -227,30 +229,45 @@ def bench_decode(args, synth, pkv):
             kern[name] = {"launches": n, "avg_us": (1e3 * ms / n) if n else 0.0}
         dec_us = 1e3 * pool.profile_samples(pkv.K_DECODE)
         pool.profile_enable(False)
+        pool.profile_kernels(None)
         dec_s = kern["decode"]["avg_us"] * 1e-6 * kern["decode"]["launches"]
         return {"elapsed": elapsed, "kv_bytes": kv_bytes, "kern": kern,
                 "gbs": kv_bytes / elapsed / 1e9, "achieved": kv_bytes / dec_s / 1e9,
                 "step_ms_pct": pct(step_ms), "decode_us_pct": pct(dec_us)}
 
-    r = run(0)
+    # Headline: only the decode kernel carries timing events (each timed
+    # launch adds two event records to the stream, ~5-10 us per step).
+    r = run(0, kernels=[pkv.K_DECODE])
     res = dict(r, wl=wl, pool=pool, seqs=seqs,
                seq_tok_s=M * args.steps / r["elapsed"])
     log("decode: %.3f ms/step, %.0f GB/s step, kernel %.1f us avg -> %.0f GB/s (%.1f%% of peak)"
         % (1e3 * r["elapsed"] / args.steps, r["gbs"], r["kern"]["decode"]["avg_us"],
            r["achieved"], 100 * r["achieved"] / HBM_PEAK_GBS))
 
+    # The same steps with every kernel timed: the per-kernel breakdown.
+    rb = run(n_steps)
+    res["breakdown"] = {
+        "ms_per_step": 1e3 * rb["elapsed"] / args.steps,
+        "kernels_us": {k: v["avg_us"] for k, v in rb["kern"].items()},
+        "step": "as the headline step, every kernel launch timed",
+    }
+    log("decode, all kernels timed: %.3f ms/step, append %.1f us, decode %.1f us, merge %.1f us"
+        % (res["breakdown"]["ms_per_step"], rb["kern"]["append"]["avg_us"],
+           rb["kern"]["decode"]["avg_us"], rb["kern"]["merge"]["avg_us"]))
+
     # The same steps with rotary embedding fused in (K turned in the append
     # scatter, Q at load in the decode kernel), base 10000.
     rope = pkv.Rope(D, math.log(10000.0), wl.max_tokens)
     pool.set_rope(rope)
-    rr = run(n_steps)
+    rr = run(2 * n_steps)
     pool.set_rope(None)
     res["rope"] = {
         "ms_per_step": 1e3 * rr["elapsed"] / args.steps,
         "gbs": rr["gbs"], "kernel_gbs": rr["achieved"],
         "kernels_us": {k: v["avg_us"] for k, v in rr["kern"].items()},
-        "step_cost_vs_plain": (r["gbs"] / rr["gbs"]) - 1.0,
-        "step": "as the headline step with a rotary table set (neox, base 1e4)",
+        "step_cost_vs_plain": (rb["gbs"] / rr["gbs"]) - 1.0,
+        "step": "as the headline step with a rotary table set (neox, base 1e4), "
+                "every kernel timed (compare with kernel_breakdown)",
     }
     log("decode + rope: %.3f ms/step, %.0f GB/s step, append %.1f us, decode %.1f us"
         % (1e3 * rr["elapsed"] / args.steps, rr["gbs"], rr["kern"]["append"]["avg_us"],
@@ -262,7 +279,8 @@ def bench_decode(args, synth, pkv):
     # only the step itself is inside the events.
     flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
     flush.sum()
-    t_first = 2 * n_steps
+    t_first = 3 * n_steps
+    pool.profile_kernels([pkv.K_DECODE])
     pool.profile_enable(True)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(COLD_STEPS)]
@@ -278,6 +296,7 @@ def bench_decode(args, synth, pkv):
     cold_ms = [a.elapsed_time(b) for a, b in ev]
     cold_dec = 1e3 * pool.profile_samples(pkv.K_DECODE)
     pool.profile_enable(False)
+    pool.profile_kernels(None)
     del flush
     res["cold"] = {
         "steps": COLD_STEPS,
@@ -650,9 +669,10 @@ def main():
         "seq_tokens_per_s": d["seq_tok_s"],
         "pct_hbm_peak": 100.0 * d["gbs"] / HBM_PEAK_GBS,
         "kv_bytes_per_step": d["kv_bytes"] / args.steps,
-        "kernels_us": {k: v["avg_us"] for k, v in d["kern"].items()},
+        "kernels_us": {k: v["avg_us"] for k, v in d["kern"].items() if v["launches"]},
         "step_ms_percentiles": d["step_ms_pct"],
         "decode_kernel_us_percentiles": d["decode_us_pct"],
+        "kernel_breakdown": d["breakdown"],
         "rope": d["rope"],
         "cold": d["cold"],
         "verify": d.get("verify"),

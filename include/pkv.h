@@ -429,6 +429,11 @@ int32_t pkv_pool_free_stack(pkv_pool *pool, int64_t *out, int32_t cap);
  * the pool launches; on == 0: stop.  Either way, clears the totals. */
 int32_t pkv_profile_enable(pkv_pool *pool, int32_t on);
 
+/* Which kernels profiling times: bit k of mask selects kernel id k (all by
+ * default).  Each timed launch adds two event records to the stream, so a
+ * caller timing one kernel of a step can leave the others untimed. */
+int32_t pkv_profile_kernels(pkv_pool *pool, uint32_t mask);
+
 /* Wait for the recorded events and report the summed kernel time (ms) and
  * launch count of one kernel id since profiling was enabled. */
 int32_t pkv_profile_read(pkv_pool *pool, int32_t kernel, double *total_ms,

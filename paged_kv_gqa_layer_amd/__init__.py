@@ -298,6 +298,11 @@ class Pool:
     def profile_enable(self, on=True):
         return _check(lib().pkv_profile_enable(self._h, int(on)), "profile_enable")
 
+    def profile_kernels(self, kernels=None):
+        """Time only the given kernel ids (None: all) while profiling is on."""
+        mask = 0xFFFFFFFF if kernels is None else sum(1 << int(k) for k in kernels)
+        return _check(lib().pkv_profile_kernels(self._h, mask), "profile_kernels")
+
     def profile_samples(self, kernel):
         """Per-launch durations (ms) of one kernel id since profiling was enabled."""
         n = lib().pkv_profile_samples(self._h, kernel, None, 0)

@@ -81,6 +81,7 @@ SIGNATURES = {
     "pkv_pool_refcounts": (_I32, [_P, _P]),
     "pkv_pool_free_stack": (_I32, [_P, _P, _I32]),
     "pkv_profile_enable": (_I32, [_P, _I32]),
+    "pkv_profile_kernels": (_I32, [_P, C.c_uint32]),
     "pkv_profile_read": (_I32, [_P, _I32, C.POINTER(C.c_double),
                                 C.POINTER(C.c_int64)]),
     "pkv_profile_samples": (_I32, [_P, _I32, _P, _I32]),

@@ -68,6 +68,7 @@ struct DeviceCtx {
   bool used = false;
 
   bool prof_on = false;
+  uint32_t prof_mask = ~0u;  // kernel ids timed while prof_on
   std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[PKV_K_COUNT];
 
   ~DeviceCtx() { release(); }
@@ -173,7 +174,7 @@ struct DeviceCtx {
     hipStream_t st;
     hipEvent_t a = nullptr, b = nullptr;
     ProfScope(DeviceCtx* c_, int k_, hipStream_t st_) : c(c_), k(k_), st(st_) {
-      if (!c->prof_on) return;
+      if (!c->prof_on || !((c->prof_mask >> k) & 1u)) return;
       if (hipEventCreate(&a) != hipSuccess) {
         a = nullptr;
         return;
@@ -1191,6 +1192,12 @@ int32_t pkv_profile_enable(pkv_pool* pool, int32_t on) {
     return PKV_ERR_DEVICE;
   pool->dev.clear_prof();
   pool->dev.prof_on = on != 0;
+  return PKV_OK;
+}
+
+int32_t pkv_profile_kernels(pkv_pool* pool, uint32_t mask) {
+  if (!pool) return PKV_ERR_BAD_ARG;
+  pool->dev.prof_mask = mask;
   return PKV_OK;
 }
 
