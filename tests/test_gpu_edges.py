@@ -231,3 +231,31 @@ def test_group_16_generic_path_and_unsupported_shapes():
     torch.cuda.synchronize()
     assert bool((out == 7.0).all())
     big.close()
+
+
+def test_profile_kernel_mask():
+    """pkv_profile_kernels limits which launches are timed."""
+    rng = np.random.default_rng(5)
+    pool = pkv.Pool(64, B, 1, G, D, max_seqs=2)
+    s = pool.seq_new(600)
+    kv = (_rand(rng, (300, G * D)), _rand(rng, (300, G * D)))
+    fill_history(pool, [s], lambda r: kv)
+    q, k, v = _rand(rng, (1, H * D)), _rand(rng, (1, G * D)), _rand(rng, (1, G * D))
+    ws = torch.empty(max(pool.decode_workspace_bytes([s], H), 4), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((1, H * D), device="cuda")
+    for kernels, timed in (([pkv.K_DECODE], {pkv.K_DECODE}),
+                           (None, {pkv.K_DECODE, pkv.K_APPEND})):
+        pool.profile_kernels(kernels)
+        pool.profile_enable(True)
+        pool.ensure_append([s], 1, check=True)
+        pool.append_layer([s], 1, 0, dev(k), dev(v), check=True)
+        pool.attn_paged_decode([s], 0, H, G, D, dev(q), SCALE, out, ws=ws, check=True)
+        pool.advance([s], 1, check=True)
+        for kid in (pkv.K_APPEND, pkv.K_DECODE):
+            ms, n = pool.profile_read(kid)
+            assert (n == 1) == (kid in timed), (kernels, kid, n)
+            assert (ms > 0) == (kid in timed)
+        pool.profile_enable(False)
+    pool.profile_kernels(None)
+    pool.close()
