@@ -130,29 +130,40 @@ class HistoryFiller:
         self.ex.shutdown()
 
 
-def kernel_code_digest(path):
-    """SHA-256 of a kernel source with its comments and blank space removed, so
+def kernel_code_digest(*paths):
+    """SHA-256 of source files with their comments and blank space removed, so
     that the digest changes with the code and not with its comments."""
     import re
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = " ".join(text.split())
-    return hashlib.sha256(text.encode()).hexdigest()
+    parts = []
+    for path in paths:
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        parts.append(" ".join(text.split()))
+    return hashlib.sha256("\n".join(parts).encode()).hexdigest()
+
+
+# The device work of a launch: the kernels, and the host code that plans and
+# launches them (split sizes, item order, grids).
+DEVICE_CODE = ("kernels.hip", "device.hpp", "api.cpp")
+
+
+def device_code_digest(csrc=None):
+    csrc = csrc or os.path.join(ROOT, "paged_kv_gqa_layer_amd", "csrc")
+    return kernel_code_digest(*[os.path.join(csrc, f) for f in DEVICE_CODE])
 
 
 def traffic_for(kernel_name, algorithmic_bytes_per_launch):
     """HBM bytes per launch implied by the committed rocprofv3 counter summary
     (its calibrated FETCH_SIZE + WRITE_SIZE over the algorithmic bytes of the
     profiled launches, times this run's algorithmic bytes per launch), if it
-    was taken on the current kernel code (comments aside); else None."""
+    was taken on the current device code (comments aside); else None."""
     path = os.path.join(ROOT, "profiles", "%s_traffic.json" % kernel_name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    src = os.path.join(ROOT, "paged_kv_gqa_layer_amd", "csrc", "kernels.hip")
-    if t.get("kernels_hip_code_sha256") != kernel_code_digest(src):
+    if t.get("device_code_sha256") != device_code_digest():
         return None
     return t["traffic_over_algorithmic"] * algorithmic_bytes_per_launch
 
@@ -557,6 +568,58 @@ def cpu_baseline_prefill(synth, oracle, n_last=16):
     }
 
 
+def bench_decode_small(args, synth, pkv):
+    """The M=32 decode workload (contexts 512-4096): the headline step at a
+    small batch, decode kernel timed by HIP events."""
+    import torch
+    n_steps = args.warmup + args.steps
+    wl = synth.decode_m32(max_steps=n_steps + 1)
+    H, G, D, M = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.M
+    pool = pkv.Pool(wl.n_blocks, wl.block_size, 1, G, D, max_seqs=M + 8)
+    pool.set_free_order(wl.free_order())
+    seqs = [pool.seq_new(wl.max_tokens) for _ in range(M)]
+    filler = HistoryFiller(wl, int(wl.ctx.max()))
+    filler.fill(pool, seqs, wl.ctx)
+    filler.close()
+    steps = [tuple(torch.from_numpy(x).cuda() for x in wl.step(t)) for t in range(n_steps)]
+    out = torch.empty((M, H * D), device="cuda")
+    seqs_np = np.asarray(seqs, np.int32)
+    wsb = int(sum(math.ceil((int(c) + n_steps + 1) / 128) for c in wl.ctx)) * H * (D + 2) * 4
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+
+    def step(t):
+        q, k, v = steps[t]
+        pool.ensure_append(seqs_np, 1, check=True)
+        pool.append_layer(seqs_np, 1, 0, k, v, check=True)
+        pool.attn_paged_decode(seqs_np, 0, H, G, D, q, wl.scale, out, ws=ws, check=True)
+        pool.advance(seqs_np, 1, check=True)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    pool.profile_kernels([pkv.K_DECODE])
+    pool.profile_enable(True)
+    t0 = time.perf_counter()
+    for t in range(args.warmup, n_steps):
+        step(t)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms, n = pool.profile_read(pkv.K_DECODE)
+    pool.profile_enable(False)
+    pool.close()
+    kv_bytes = sum(int((wl.ctx.astype(np.int64) + t + 1).sum()) * 2 * wl.kv_dim * 4
+                   for t in range(args.warmup, n_steps))
+    res = {
+        "workload": wl.name, "M": M, "ms_per_step": 1e3 * elapsed / args.steps,
+        "gbs": kv_bytes / elapsed / 1e9, "kernel_us": 1e3 * ms / n,
+        "kernel_gbs": kv_bytes / (ms * 1e-3) / 1e9, "seq_tokens_per_s": M * args.steps / elapsed,
+        "step": "ensure_append + append_layer + attn_paged_decode + advance",
+    }
+    log("decode M=32: %.3f ms/step, %.0f GB/s step, kernel %.1f us -> %.0f GB/s"
+        % (res["ms_per_step"], res["gbs"], res["kernel_us"], res["kernel_gbs"]))
+    return res
+
+
 def bench_prefill(args, synth, pkv):
     import torch
     wl = synth.prefill_8x3584p512()
@@ -662,7 +725,7 @@ def main():
             "block_size": wl.block_size, "layers": 1,
             "context_rows": [int(wl.ctx.min()), int(wl.ctx.max())],
             "mean_total_k": float(wl.ctx.mean() + 1 + args.warmup + (args.steps - 1) / 2),
-            "split_keys": "512 / 1024 / 2048 for rows below 4096 / 8192 / above",
+            "split_keys": "256 / 512 / 1024 / 2048 for rows below 2048 / 4096 / 8192 / above",
             "placement": "random permutation",
             "step": "ensure_append + append_layer + attn_paged_decode + advance",
         },
@@ -687,6 +750,8 @@ def main():
     d["pool"].close()
     del d
     torch.cuda.empty_cache()
+    if args.workload == "decode_m256":
+        line["decode_m32"] = bench_decode_small(args, synth, pkv)
     if not args.no_prefill:
         line["prefill"] = bench_prefill(args, synth, pkv)
     if not args.no_forked:

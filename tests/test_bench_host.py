@@ -16,6 +16,7 @@ def test_code_digest_ignores_comments_only(tmp_path):
     b.write_text("/* another\n   header */\nint f(int x) {   return x + 1; }\n")
     c.write_text("int f(int x) {\n  return x + 2;\n}\n")
     assert bench.kernel_code_digest(a) == bench.kernel_code_digest(b)
+    assert bench.kernel_code_digest(a, c) != bench.kernel_code_digest(c, a)
     assert bench.kernel_code_digest(a) != bench.kernel_code_digest(c)
 
 
