@@ -725,7 +725,7 @@ def main():
             "block_size": wl.block_size, "layers": 1,
             "context_rows": [int(wl.ctx.min()), int(wl.ctx.max())],
             "mean_total_k": float(wl.ctx.mean() + 1 + args.warmup + (args.steps - 1) / 2),
-            "split_keys": "256 / 512 / 1024 / 2048 for rows below 2048 / 4096 / 8192 / above",
+            "split_keys": "256 / 512 / 1024 / 2048 for rows below 2048 / 6144 / 8192 / above",
             "placement": "random permutation",
             "step": "ensure_append + append_layer + attn_paged_decode + advance",
         },

@@ -234,7 +234,7 @@ size_t pkv_decode_workspace_bytes(pkv_pool *pool, const int32_t *seqs,
  * key is visible.  Q_dev, out_dev: [M, n_heads * head_dim], row r for
  * seqs[r].  Long contexts are split into key ranges whose size follows from
  * the sequence's own length alone (256 rows below 2048 keys, 512 below
- * 4096, 1024 below 8192, 2048 above) and whose partial softmax states are merged in a fixed
+ * 6144, 1024 below 8192, 2048 above) and whose partial softmax states are merged in a fixed
  * order, so each output depends only on its own sequence (independent of M,
  * batch order and placement).
  * ws_dev: >= pkv_decode_workspace_bytes bytes (may be NULL when that is 0).

@@ -69,7 +69,7 @@ struct ContigMap {
   }
 };
 
-// Key split of the decode kernels for rows of 2048-4095 keys (splits are
+// Key split of the decode kernels for rows of 2048-6143 keys (splits are
 // multiples of the 16-row page).
 constexpr int32_t kDecodeSplit = 512;
 // Own keys per split in a shared-prefix decode plan: a forked row's own keys
@@ -78,15 +78,19 @@ constexpr int32_t kDecodeSplit = 512;
 constexpr int32_t kSharedOwnSplit = 128;
 // Own keys per split of one row, from the row's own key count alone (so a
 // row's result does not depend on the rest of the batch): 256 below 2048
-// keys, 512 below 4096, 1024 below 8192, 2048 above -- longer rows take
+// keys, 512 below 6144, 1024 below 8192, 2048 above -- longer rows take
 // longer splits, which cuts the per-wave start-up, partial writes and merge
 // reads, while short rows keep enough waves to fill the GPU in small
-// batches -- doubled for more than 4 queries per row (each key costs more
-// work), and the shared own-key split in a shared-prefix plan.
+// batches.  A wave streams at a latency-bound rate, so in a small batch the
+// longest split sets the kernel time: rows of 4-6K keys keep 512-key splits
+// (1024 there made a 32-row batch of such rows 35% slower, and the 512 costs
+// a large batch well under 1%).  Doubled for more than 4 queries per row
+// (each key costs more work); the shared own-key split in a shared-prefix
+// plan.
 inline int32_t split_keys(int64_t own, int32_t n_q, bool shared = false) {
   if (shared) return kSharedOwnSplit;
   const int32_t s = own >= 8192   ? 4 * kDecodeSplit
-                    : own >= 4096 ? 2 * kDecodeSplit
+                    : own >= 6144 ? 2 * kDecodeSplit
                     : own >= 2048 ? kDecodeSplit
                                   : kDecodeSplit / 2;
   return n_q <= 4 ? s : 2 * s;

@@ -672,8 +672,12 @@ __device__ __forceinline__ void mq_attend(const Map& m, const RowDesc& rd,
     ps += __shfl_xor(ps, 32);
     l_run = fmaf(l_run, alpha, ps);
     m_run = m_new;
+    // alpha is exactly 1 for a row whose maximum did not move: skip the
+    // rescale when that holds for every row of the wave
+    if (__ballot(alpha != 1.f)) {
 #pragma unroll
-    for (int b = 0; b < 8; ++b) Ot[b] *= alpha;
+      for (int b = 0; b < 8; ++b) Ot[b] *= alpha;
+    }
   };
   // PV step s: key 4s + mq; va / vb: dims 4c + e and 64 + 4c + e
   auto pv_step = [&](const floatx4& P, int s, const float4& va, const float4& vb) {

@@ -1,5 +1,5 @@
-"""GPU parity at the edges of the size range: one very long sequence (128
-splits of 512 keys) beside a short one in decode, verify and prefill; a
+"""GPU parity at the edges of the size range: one very long sequence (33
+splits of 2048 keys) beside a short one in decode, verify and prefill; a
 single-sequence batch; a 1024-sequence batch of short contexts.  Outputs are
 checked against the oracle (sampled where the oracle would be slow) at
 1e-4 + 1e-4 * |oracle|, and against the contiguous twin bit for bit."""

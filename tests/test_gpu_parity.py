@@ -200,8 +200,9 @@ def test_decode_batch_and_placement_invariance():
 
 
 @pytest.mark.parametrize("ctx", [0, 1, 15, 16, 17, 255, 256, 511, 512, 513, 1023, 1535,
-                                 2046, 2047,
-                                 4094, 4095, 4096, 8190, 8191, 8192, 16383])
+                                 2046, 2047, 2048,
+                                 4094, 4095, 4096, 6142, 6143, 6144, 8190, 8191, 8192,
+                                 16383])
 def test_decode_lengths_around_page_and_split_edges(ctx):
     H, G, D = 32, 8, 128
     rng = np.random.default_rng(ctx)
