@@ -207,3 +207,37 @@ def test_binding_rejects_host_and_malformed_buffers():
         pkv._dptr(torch.empty(4, dtype=torch.float32), "Q")
     assert pkv._ws(None) == (None, 0)
     assert pkv._dptr(None, "Q") is None
+
+
+def _split(own, n_q):
+    """The documented key split of a row with `own` keys and n_q new rows."""
+    s = 256 if own < 2048 else 512 if own < 6144 else 1024 if own < 8192 else 2048
+    return s if n_q <= 4 else 2 * s
+
+
+@pytest.mark.parametrize("n_q", [1, 4, 8])
+def test_split_plan_sizes(n_q):
+    """Workspace sizes (partial slots x n_q x heads x (head_dim + 2) floats)
+    follow the per-row split sizes at every threshold; a batch needs the sum
+    of its rows' slots, independent of order."""
+    L = pkv.lib()
+    H, G, D = 32, 8, 128
+    per_slot = n_q * H * (D + 2) * 4
+
+    def ws(lens):
+        a = np.asarray(lens, np.int32)
+        p = a.ctypes.data_as(pkv._lib.C.c_void_p)
+        if n_q == 1:
+            return L.pkv_contig_decode_workspace_bytes(p, a.size, H, G, D)
+        return L.pkv_contig_verify_workspace_bytes(p, a.size, n_q, H, G, D)
+
+    edges = [0, 255, 256, 511, 2047 - n_q, 2048 - n_q, 2049 - n_q, 6143 - n_q, 6144 - n_q,
+             6145 - n_q, 8191 - n_q, 8192 - n_q, 12288, 16383, 65536]
+    slots = []
+    for seq_len in edges:
+        own = seq_len + n_q
+        k = -(-own // _split(own, n_q))
+        slots.append(k)
+        assert ws([seq_len]) == (k * per_slot if k > 1 else 0), seq_len
+    assert ws(edges) == sum(slots) * per_slot
+    assert ws(edges[::-1]) == sum(slots) * per_slot
