@@ -72,6 +72,15 @@ __device__ __forceinline__ float4 ld4_stream(const float* p) {
   const f32x4 r = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
   return make_float4(r.x, r.y, r.z, r.w);
 }
+// Streaming store: the decode kernel's split partials are read once, by the
+// merge launch; written with the non-temporal hint they do not take L2 lines
+// from the K/V stream (the decode launch is 1% faster, the merge 2 us
+// slower).  The verify kernel's partials stay ordinary stores: streaming
+// them made it slower.
+__device__ __forceinline__ void st4_stream(float* p, float4 v) {
+  const f32x4 r = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(r, reinterpret_cast<f32x4*>(p));
+}
 
 __device__ __forceinline__ float dot8(const float4& ka, const float4& kb,
                                       const float (&qa)[4],
@@ -481,13 +490,11 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
     for (int j = 0; j < GROUP; ++j) {
       if ((j & 3) == rr) {
         float* po = a.part_o + (hbase + j) * D;
-        *reinterpret_cast<float4*>(po + 4 * c) =
-            make_float4(oa[j][0], oa[j][1], oa[j][2], oa[j][3]);
-        *reinterpret_cast<float4*>(po + 64 + 4 * c) =
-            make_float4(ob[j][0], ob[j][1], ob[j][2], ob[j][3]);
+        st4_stream(po + 4 * c, make_float4(oa[j][0], oa[j][1], oa[j][2], oa[j][3]));
+        st4_stream(po + 64 + 4 * c, make_float4(ob[j][0], ob[j][1], ob[j][2], ob[j][3]));
         if (c == 0) {
-          a.part_ml[(hbase + j) * 2 + 0] = mrun[j];
-          a.part_ml[(hbase + j) * 2 + 1] = Lf[j];
+          __builtin_nontemporal_store(mrun[j], a.part_ml + (hbase + j) * 2 + 0);
+          __builtin_nontemporal_store(Lf[j], a.part_ml + (hbase + j) * 2 + 1);
         }
       }
     }
