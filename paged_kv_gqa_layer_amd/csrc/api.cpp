@@ -70,6 +70,9 @@ struct DeviceCtx {
   bool prof_on = false;
   uint32_t prof_mask = ~0u;  // kernel ids timed while prof_on
   std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[PKV_K_COUNT];
+  // Timing events of earlier profiling runs, reused (creating timing events
+  // can cost the host more than a short step).
+  std::vector<hipEvent_t> ev_pool;
 
   ~DeviceCtx() { release(); }
 
@@ -85,17 +88,30 @@ struct DeviceCtx {
       b = DevBuf();
     }
     clear_prof();
+    for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+    ev_pool.clear();
     used = false;
   }
 
+  // Callers synchronise the stream first, so every recorded event is done.
   void clear_prof() {
     for (auto& v : prof_ev) {
       for (auto& e : v) {
-        (void)hipEventDestroy(e.first);
-        (void)hipEventDestroy(e.second);
+        ev_pool.push_back(e.first);
+        ev_pool.push_back(e.second);
       }
       v.clear();
     }
+  }
+
+  hipEvent_t take_event() {
+    if (!ev_pool.empty()) {
+      const hipEvent_t e = ev_pool.back();
+      ev_pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    return hipEventCreate(&e) == hipSuccess ? e : nullptr;
   }
 
   // All device work of a context goes to one stream at a time.
@@ -175,12 +191,9 @@ struct DeviceCtx {
     hipEvent_t a = nullptr, b = nullptr;
     ProfScope(DeviceCtx* c_, int k_, hipStream_t st_) : c(c_), k(k_), st(st_) {
       if (!c->prof_on || !((c->prof_mask >> k) & 1u)) return;
-      if (hipEventCreate(&a) != hipSuccess) {
-        a = nullptr;
-        return;
-      }
-      if (hipEventCreate(&b) != hipSuccess) {
-        (void)hipEventDestroy(a);
+      if (!(a = c->take_event())) return;
+      if (!(b = c->take_event())) {
+        c->ev_pool.push_back(a);
         a = nullptr;
         return;
       }

@@ -237,20 +237,47 @@ __device__ __forceinline__ void merge_head(const AttnArgs& a, int32_t row,
   const int64_t H = a.n_heads;
   const int64_t SH = (int64_t)a.n_q * H;  // entries per slot
   const int64_t h0 = (int64_t)part_base * SH + (int64_t)qi * H + head;
-  float mx = kNegInf;
-  for (int32_t s = lane; s < nsp; s += 64) mx = fmaxf(mx, a.part_ml[(h0 + s * SH) * 2]);
+  const float* obase = a.part_o + h0 * D + 2 * lane;
+  // One round of loads before any arithmetic: this lane's split statistics
+  // and the first U partial rows (most rows have at most U splits).
+  float m_first = kNegInf, l_first = 0.f;
+  if (lane < nsp) {
+    const float2 ml = *reinterpret_cast<const float2*>(a.part_ml + (h0 + lane * SH) * 2);
+    m_first = ml.x;
+    l_first = ml.y;
+  }
+  float2 ov0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    ov0[u] = u < nsp ? *reinterpret_cast<const float2*>(obase + (int64_t)u * SH * D)
+                     : make_float2(0.f, 0.f);
+  float mx = m_first;
+  for (int32_t s = lane + 64; s < nsp; s += 64) mx = fmaxf(mx, a.part_ml[(h0 + s * SH) * 2]);
   mx = wave_max(mx);
   float lw = 0.f, o0 = 0.f, o1 = 0.f;
   for (int32_t s0 = 0; s0 < nsp; s0 += 64) {
     const int32_t s = s0 + lane;
     float w = 0.f;
     if (s < nsp) {
-      w = fast_exp2(a.part_ml[(h0 + s * SH) * 2] - mx);
-      lw = fmaf(w, a.part_ml[(h0 + s * SH) * 2 + 1], lw);
+      const float ms = s0 == 0 ? m_first : a.part_ml[(h0 + s * SH) * 2];
+      const float ls = s0 == 0 ? l_first : a.part_ml[(h0 + s * SH) * 2 + 1];
+      w = fast_exp2(ms - mx);
+      lw = fmaf(w, ls, lw);
     }
     const int32_t cnt = min(64, nsp - s0);
-    const float* base = a.part_o + (h0 + (int64_t)s0 * SH) * D + 2 * lane;
+    const float* base = obase + (int64_t)s0 * SH * D;
     int32_t t = 0;
+    if (s0 == 0) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wt = __shfl(w, u);
+        if (u < cnt) {
+          o0 = fmaf(wt, ov0[u].x, o0);
+          o1 = fmaf(wt, ov0[u].y, o1);
+        }
+      }
+      t = min(U, cnt);
+    }
     for (; t + U <= cnt; t += U) {
       float2 ov[U];
 #pragma unroll
