@@ -175,6 +175,21 @@ def test_attention_front_checks_order():
     pre = L.pkv_attn_paged_prefill
     assert pre(p._h, sp, 1, 0, 0, 4, 2, 4, None, 1, 1.0, None, None) == pkv.BAD_DIM
     assert pre(p._h, sp, 1, 2, 0, 6, 4, 4, None, 1, 1.0, None, None) == pkv.BAD_GQA
+    fused = L.pkv_attn_with_paged_decode
+    assert fused(p._h, sp, 0, 0, 4, 2, 4, None, None, None, 1.0, None, None, 0,
+                 None) == pkv.BAD_DIM
+    assert fused(p._h, sp, 1, 0, 3, 2, 4, None, None, None, 1.0, None, None, 0,
+                 None) == pkv.BAD_GQA
+    assert fused(p._h, bad.ctypes.data_as(pkv._lib.C.c_void_p), 1, 0, 4, 2, 4, None,
+                 None, None, 1.0, None, None, 0, None) == pkv.ERR_SEQ
+    assert fused(p._h, sp, 1, 1, 4, 2, 4, None, None, None, 1.0, None, None, 0,
+                 None) == pkv.BAD_ARG
+    # rows not ensured, then (ensured) a metadata-only pool cannot attend
+    assert fused(p._h, sp, 1, 0, 4, 2, 4, None, None, None, 1.0, None, None, 0,
+                 None) == pkv.ERR_SEQ
+    assert p.ensure_append(s, 1) == 0
+    assert fused(p._h, sp, 1, 0, 4, 2, 4, None, None, None, 1.0, None, None, 0,
+                 None) == pkv.BAD_ARG
 
 
 def test_rope_table_argument_checks():
