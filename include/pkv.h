@@ -253,22 +253,20 @@ int32_t pkv_attn_paged_decode(pkv_pool *pool, const int32_t *seqs, int32_t M,
 
 /* Append, then attend, for one new row per sequence: the pages' per-layer
  * wrapper (append this layer's K/V rows, then paged GQA attention over
- * every row including the new one) as one call.  Equivalent to
+ * every row including the new one) as one call.  It runs
  * pkv_append_layer(pool, seqs, M, 1, layer, K_new_dev, V_new_dev, stream)
- * followed by pkv_attn_paged_decode(...) with the same arguments: the pool
- * holds the same bytes and out_dev the same bits afterwards.  For head_dim
- * 128, 16-row pages and group 1, 2, 4 or 8 both happen in one kernel launch
- * (the wave that reads a row's last key split stores the new row first);
- * other shapes run the two launches.  K_new_dev, V_new_dev:
- * [M, n_kv_heads * head_dim], row r for seqs[r]; Q_dev, out_dev as for
- * pkv_attn_paged_decode; ws_dev: >= pkv_decode_workspace_bytes bytes.
- * Rows must be ensured (pkv_ensure_append(.., 1, ..)) and not yet advanced.
+ * and then pkv_attn_paged_decode(...) with the same arguments (the same
+ * launches, so the same pool bytes and output bits), after checking the
+ * arguments of both.  K_new_dev, V_new_dev: [M, n_kv_heads * head_dim], row
+ * r for seqs[r]; Q_dev, out_dev as for pkv_attn_paged_decode; ws_dev:
+ * >= pkv_decode_workspace_bytes bytes.  Rows must be ensured
+ * (pkv_ensure_append(.., 1, ..)) and not yet advanced.
  * Errors, in the pages' order: BAD_DIM (M, n_heads, n_kv_heads, head_dim
  * <= 0, or head shape != the pool's), BAD_GQA, SEQ (bad or repeated id),
  * then BAD_ARG (layer out of range), SEQ (rows not ensured, or a target
  * block shared), CAPACITY (rotary table too short), BAD_ARG (metadata-only
  * pool, NULL pointer, workspace too small), DEVICE.  Nothing is launched on
- * an error.
+ * an argument error.
  * ("nx_f32_attn_paged.nx source": nx_f32_attn_with_paged -- append, then
  * attention per query head -- with n_q = 1.) */
 int32_t pkv_attn_with_paged_decode(pkv_pool *pool, const int32_t *seqs,

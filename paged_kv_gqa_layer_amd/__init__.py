@@ -233,7 +233,7 @@ class Pool:
                                Q, K_new, V_new, scale, out, ws=None, stream=None,
                                check=False):
         """append_layer of one row per sequence, then attn_paged_decode, as
-        one call (one launch for the decode kernel's shapes)."""
+        one call (the pages' append-then-attend wrapper)."""
         a = _ids(seqs)
         q_dim = n_heads * head_dim
         kv_dim = n_kv_heads * head_dim

@@ -416,7 +416,6 @@ struct pkv_pool {
   bool last_shared = false;        // the last attention call grouped prefixes
   int32_t shared_heads = 0;        // ... with this many query heads per kv head
   SharedPlan shared;
-  std::vector<uint8_t> in_batch;   // scratch: sequence ids of the current call
 
   pkv_pool(int32_t nb, int32_t bs, int32_t nl, int32_t g, int32_t d, int32_t ms)
       : meta(nb, bs, nl, g, d, ms) {}
@@ -588,7 +587,7 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
                       int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
                       int32_t n_q, int32_t causal, float scale, int32_t M,
                       int32_t block_size, Kind kind, const double2* rope,
-                      hipStream_t st, const pkv::NewRows* nr = nullptr) {
+                      hipStream_t st) {
   const int32_t group = n_heads / n_kv_heads;
   AttnArgs a;
   a.rows = reinterpret_cast<const RowDesc*>(rows_dev);
@@ -629,15 +628,8 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
     {
       const bool one = n_q == 1 && pkv::fast_decode_ok(head_dim, group, block_size);
       DeviceCtx::ProfScope ps(&dev, one ? PKV_K_DECODE : PKV_K_VERIFY, st);
-      if constexpr (std::is_same<Map, PagedMap>::value) {
-        if (nr && one) e = pkv::launch_decode_append(map, a, *nr, group, st);
-        else if (nr) e = hipErrorInvalidValue;
-        else e = one ? pkv::launch_decode_fast(map, a, group, st)
-                     : pkv::launch_verify_mfma(map, a, group, st);
-      } else {
-        e = one ? pkv::launch_decode_fast(map, a, group, st)
-                : pkv::launch_verify_mfma(map, a, group, st);
-      }
+      e = one ? pkv::launch_decode_fast(map, a, group, st)
+              : pkv::launch_verify_mfma(map, a, group, st);
       if (e != hipSuccess) return PKV_ERR_DEVICE;
     }
     if (pl.max_parts <= 1) return PKV_OK;
@@ -893,20 +885,6 @@ int32_t shared_heads_for(const pkv_pool* pool, Kind kind, int32_t n_heads) {
   return group;
 }
 
-// Whether a pending page-table patch names a page a decode launch over
-// seqs reads through the mirror (a page before the one the new rows land
-// in, e.g. every page of a fresh fork); those must be applied before it.
-bool patches_read_by_decode(pkv_pool* p, const int32_t* seqs, int32_t M) {
-  const auto& pt = p->meta.patches();
-  if (pt.empty()) return false;
-  const int32_t B = p->meta.block_size();
-  p->in_batch.assign(static_cast<size_t>(p->meta.max_seqs()), 0);
-  for (int32_t r = 0; r < M; ++r) p->in_batch[seqs[r]] = 1;
-  for (const auto& q : pt)
-    if (p->in_batch[q.seq] && q.page < p->meta.seq(q.seq)->seq_len / B) return true;
-  return false;
-}
-
 size_t pool_workspace_bytes(pkv_pool* pool, const int32_t* seqs, int32_t M,
                             int32_t n_q, int32_t n_heads, Kind kind) {
   if (!pool || M <= 0 || n_q <= 0 || n_heads <= 0) return static_cast<size_t>(-1);
@@ -1010,6 +988,8 @@ int32_t pkv_attn_with_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t 
                                    const float* K_new_dev, const float* V_new_dev,
                                    float scale, float* out_dev, void* ws_dev,
                                    size_t ws_bytes, void* stream) {
+  // every check of both calls first, in the pages' order, so an error
+  // leaves the pool as it was
   if (!pool) return PKV_ERR_BAD_ARG;
   if (int32_t rc = attn_front_checks(M, 1, n_heads, n_kv_heads, head_dim)) return rc;
   const auto& m = pool->meta;
@@ -1022,29 +1002,10 @@ int32_t pkv_attn_with_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t 
   if (!Q_dev || !out_dev || !K_new_dev || !V_new_dev) return PKV_ERR_BAD_ARG;
   const size_t need = pool_workspace_bytes(pool, seqs, M, 1, n_heads, Kind::kDecode);
   if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
-  if (!pkv::fast_decode_ok(head_dim, n_heads / n_kv_heads, m.block_size())) {
-    // other shapes: the append launch, then the attention launch
-    if (int32_t rc = pkv_append_layer(pool, seqs, M, 1, layer, K_new_dev, V_new_dev, stream))
-      return rc;
-    return pkv_attn_paged_decode(pool, seqs, M, layer, n_heads, n_kv_heads, head_dim,
-                                 Q_dev, scale, out_dev, ws_dev, ws_bytes, stream);
-  }
-  const hipStream_t st = as_stream(stream);
-  if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
-  pool->last_shared = false;
-  pool->shared_heads = 0;
-  if (size_mirror(pool, st) != hipSuccess) return PKV_ERR_DEVICE;
-  // patches the decode waves do not read go with the launch
-  pkv::PatchArgs pa{};
-  const bool early = patches_read_by_decode(pool, seqs, M);
-  const int32_t* rows = nullptr;
-  if (pool_rows(pool, seqs, M, 1, 0, st, &rows, early ? nullptr : &pa) != hipSuccess)
-    return PKV_ERR_DEVICE;
-  const pkv::NewRows nr{K_new_dev, V_new_dev, pa};
-  const PagedMap pm = make_paged_map(pool, layer);
-  return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, ws_dev, n_heads,
-                       n_kv_heads, head_dim, 1, 1, scale, M, m.block_size(), Kind::kDecode,
-                       rope_table(pool->rope), st, &nr);
+  if (int32_t rc = pkv_append_layer(pool, seqs, M, 1, layer, K_new_dev, V_new_dev, stream))
+    return rc;
+  return pkv_attn_paged_decode(pool, seqs, M, layer, n_heads, n_kv_heads, head_dim, Q_dev,
+                               scale, out_dev, ws_dev, ws_bytes, stream);
 }
 
 int32_t pkv_attn_paged_verify(pkv_pool* pool, const int32_t* seqs, int32_t M,

@@ -181,22 +181,6 @@ hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
 hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);
-// This layer's new rows, one per sequence ([M, n_kv_heads * head_dim]), for
-// a decode launch that appends them itself, and the pending mirror patches
-// it applies (none of which may name a page its waves read through the
-// mirror).
-struct NewRows {
-  const float* K;
-  const float* V;
-  PatchArgs pa;
-};
-// decode_fast that also appends: the wave of the split holding the new key
-// stores that key's K (turned when a rotary table is set) and V at its place
-// in the row's append block and uses them without loading them back; the
-// last page of each row is addressed through append_block.  The outputs
-// are bit-identical to launch_append_one followed by launch_decode_fast.
-hipError_t launch_decode_append(const PagedMap& m, const AttnArgs& a,
-                                const NewRows& nr, int32_t group, hipStream_t st);
 // Split multi-query decode (n_q x group <= kVerifyMaxRows), then launch_merge.
 hipError_t launch_verify_mfma(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);

@@ -303,12 +303,11 @@ __device__ __forceinline__ void merge_head(const AttnArgs& a, int32_t row,
 }
 
 // One wave's work: work item item_idx (a (row, split) pair), kv head kvh;
-// lane = this thread's lane in its wave.  APPEND: the rows' new keys come
-// from nr and are stored by the wave of the split that holds them.
-template <int GROUP, class Map, bool APPEND = false>
+// lane = this thread's lane in its wave.
+template <int GROUP, class Map>
 __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
                                             int32_t item_idx, int32_t kvh,
-                                            int lane, const NewRows& nr = NewRows{}) {
+                                            int lane) {
   constexpr int D = 128;
   constexpr int B = 16;
   constexpr int NI = B / 4;
@@ -325,37 +324,6 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
   const int32_t k_end = min(total_k, k_begin + rd.split);
   const int32_t p_begin = k_begin / B;
   const int32_t p_end = (k_end + B - 1) / B;
-  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
-
-  // APPEND: the split ending at total_k holds the new key total_k - 1 (page
-  // p_new, position t_new).  Before reading any page, its wave stores the
-  // key's K (turned at the key's position, as an append turns it) and V from
-  // the new rows into the row's append block, each value by the lane that
-  // later loads it, so the load returns it (one thread's store and load of
-  // an address stay in order).  Page p_new is addressed through
-  // append_block: its mirror entry may still be a pending patch.
-  const bool has_new = APPEND && k_end == total_k;
-  const int32_t p_new = (total_k - 1) / B;
-  const int32_t t_new = total_k - 1 - p_new * B;
-  if constexpr (APPEND) {
-    if (has_new && rr == (t_new & 3)) {
-      const int64_t src = ((int64_t)row * a.n_kv_heads + kvh) * D + 4 * c;
-      float4 ka = ld4(nr.K + src), kb = ld4(nr.K + src + 64);
-      const float4 va = ld4(nr.V + src), vb = ld4(nr.V + src + 64);
-      if (a.rope) {
-        const double2* cr = a.rope + (int64_t)(total_k - 1) * (D / 2) + 4 * c;
-        rotate_pair(ka.x, kb.x, cr[0]);
-        rotate_pair(ka.y, kb.y, cr[1]);
-        rotate_pair(ka.z, kb.z, cr[2]);
-        rotate_pair(ka.w, kb.w, cr[3]);
-      }
-      float* dst = m.block(rd.append_block, kvh) + t_new * D + 4 * c;
-      *reinterpret_cast<float4*>(dst) = ka;
-      *reinterpret_cast<float4*>(dst + 64) = kb;
-      *reinterpret_cast<float4*>(dst + m.v_off) = va;
-      *reinterpret_cast<float4*>(dst + m.v_off + 64) = vb;
-    }
-  }
 
   float qa[GROUP][4], qb[GROUP][4];
   {
@@ -404,14 +372,11 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
     for (int e = 0; e < 4; ++e) oa[j][e] = ob[j][e] = 0.f;
   }
 
+  const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
   float4 kA[NI], kB[NI], vA[NI], vB[NI];
   auto load_page = [&](int32_t p, float4(&ka)[NI], float4(&kb)[NI],
                        float4(&va)[NI], float4(&vb)[NI]) {
-    const float* kp;
-    if constexpr (APPEND)
-      kp = has_new && p == p_new ? m.block(rd.append_block, kvh) : m.page(rd, p, kvh);
-    else
-      kp = m.page(rd, p, kvh);
+    const float* kp = m.page(rd, p, kvh);
     const float* vp = kp + m.v_off;
     const int32_t n_valid = min(B, k_end - p * B);
 #pragma unroll
@@ -561,24 +526,6 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
       }
     }
   }
-}
-
-// Decode that also appends the rows' new K/V (one per sequence); the first
-// threads apply the pending page-table patches, none of which names a page
-// the waves read through the mirror.
-// Two waves per SIMD as the plain decode kernel has (the compiler would
-// otherwise trade one for registers; group 8 fits only one either way).
-template <int GROUP>
-__global__ __launch_bounds__(64)
-__attribute__((amdgpu_waves_per_eu(GROUP == 8 ? 1 : 2, 2)))
-void decode_append_kernel(PagedMap m, AttnArgs a, NewRows nr) {
-  for (int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x; i < nr.pa.n;
-       i += (int64_t)gridDim.x * 64)
-    nr.pa.mirror[nr.pa.patches[3 * i] * nr.pa.stride + nr.pa.patches[3 * i + 1]] =
-        nr.pa.patches[3 * i + 2];
-  const int32_t item_idx = blockIdx.x / a.n_kv_heads;
-  decode_wave<GROUP, PagedMap, true>(m, a, item_idx, blockIdx.x - item_idx * a.n_kv_heads,
-                                     threadIdx.x, nr);
 }
 
 template <int GROUP, class Map>
@@ -1409,19 +1356,6 @@ hipError_t decode_fast_impl(const Map& m, const AttnArgs& a, int32_t group,
   return hipGetLastError();
 }
 
-hipError_t decode_append_impl(const PagedMap& m, const AttnArgs& a, const NewRows& nr,
-                              int32_t group, hipStream_t st) {
-  const dim3 grid(a.n_items * a.n_kv_heads);
-  switch (group) {
-    case 1: decode_append_kernel<1><<<grid, 64, 0, st>>>(m, a, nr); break;
-    case 2: decode_append_kernel<2><<<grid, 64, 0, st>>>(m, a, nr); break;
-    case 4: decode_append_kernel<4><<<grid, 64, 0, st>>>(m, a, nr); break;
-    case 8: decode_append_kernel<8><<<grid, 64, 0, st>>>(m, a, nr); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 template <class Map>
 hipError_t verify_impl(const Map& m, const AttnArgs& a, int32_t group,
                        hipStream_t st) {
@@ -1538,10 +1472,6 @@ hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,
 hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st) {
   return decode_fast_impl(m, a, group, st);
-}
-hipError_t launch_decode_append(const PagedMap& m, const AttnArgs& a,
-                                const NewRows& nr, int32_t group, hipStream_t st) {
-  return decode_append_impl(m, a, nr, group, st);
 }
 hipError_t launch_verify_mfma(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st) {

@@ -1,14 +1,14 @@
 """GPU: the append-then-attend call (pkv_attn_with_paged_decode, the pages'
 per-layer wrapper "nx_f32_attn_with_paged" with one new row per sequence)
-against the two calls it replaces, pkv_append_layer + pkv_attn_paged_decode,
+against the two calls it stands for, pkv_append_layer + pkv_attn_paged_decode,
 on twin pools (same placement, same history, same operations).
 
-Bars: outputs bit-identical at every step; the pools' used blocks
-bit-identical afterwards; reference counts and page tables identical; one
-step checked against the oracle at 1e-4 + 1e-4 * |oracle|.  Cases: GQA
+Bars: outputs bit-identical at every step; every written position of the
+pools bit-identical afterwards; reference counts and page tables identical;
+one step checked against the oracle at 1e-4 + 1e-4 * |oracle|.  Cases: GQA
 groups 1, 2, 4, 8 over page boundaries, rotary table on, two layers per
 step, forks (a fork's pending page-table entries and the copy of a shared
-tail), a shape the one-launch form does not cover, and the error path.
+tail), the generic kernel's shapes, and the error path (nothing launched).
 """
 import math
 
@@ -170,7 +170,7 @@ def test_fused_after_fork_and_copy_on_append():
     _same_pools(pa, sa2, pb, sb2)
 
 
-def test_fused_other_shape_runs_two_launches():
+def test_fused_generic_shape():
     # head_dim 64: the generic kernel; same contract
     (pa, sa), (pb, sb) = _twins([3, 90, 300], 4, 64, seed=9)[0]
     rng = np.random.default_rng(10)
