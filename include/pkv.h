@@ -19,6 +19,7 @@
  *     pkv_append_layer(batch, n, layer, K_new, V_new)
  *     pkv_attn_paged_decode(...)           (n == 1)  or
  *     pkv_attn_paged_prefill(..., n_q = n)
+ *     (for n == 1 both lines may be one pkv_attn_with_paged_decode(...))
  *   pkv_advance(batch, n)                  once per step, after all layers
  *
  * Conventions.
