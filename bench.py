@@ -743,7 +743,7 @@ def main():
             "bound": "hbm", "achieved": d["achieved"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": d["achieved"] / HBM_PEAK_GBS,
             "traffic": (traffic if traffic is not None else None),
-            "kernel": "decode_fast_kernel<4, PagedMap>",
+            "kernel": "decode_fast_kernel<4, PagedMap, true>",
             "bytes_per_launch": d["kv_bytes"] / args.steps,
         },
     }

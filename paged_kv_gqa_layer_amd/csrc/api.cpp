@@ -222,6 +222,7 @@ struct RowPlan {
   int32_t n_items = 0;      // split decode items (the rows' own key splits)
   int32_t n_slots = 0;      // partial-result slots (own splits + prefix splits)
   int32_t max_parts = 0;    // most partial results of one row
+  int32_t max_split = 0;    // longest split (keys)
   size_t item_off = 0;      // int32 offset of the (row, split) item list
   // shared-prefix decode (empty otherwise): int32 offsets in the blob
   int32_t n_pre_items = 0;
@@ -269,6 +270,7 @@ RowPlan build_rows(std::vector<int32_t>& v, int32_t M, int32_t n_q, bool shared,
     pl.n_items += nsp;
     pl.n_slots += in.n_pre + nsp;
     pl.max_parts = std::max(pl.max_parts, in.n_pre + nsp);
+    pl.max_split = std::max(pl.max_split, split);
     if (rem) tails.emplace_back(rem, r);
     if (std::find(sizes.begin(), sizes.end(), split) == sizes.end()) sizes.push_back(split);
   }
@@ -628,7 +630,8 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
     {
       const bool one = n_q == 1 && pkv::fast_decode_ok(head_dim, group, block_size);
       DeviceCtx::ProfScope ps(&dev, one ? PKV_K_DECODE : PKV_K_VERIFY, st);
-      e = one ? pkv::launch_decode_fast(map, a, group, st)
+      e = one ? pkv::launch_decode_fast(map, a, group,
+                                        pl.max_split >= 4 * pkv::kDecodeSplit, st)
               : pkv::launch_verify_mfma(map, a, group, st);
       if (e != hipSuccess) return PKV_ERR_DEVICE;
     }

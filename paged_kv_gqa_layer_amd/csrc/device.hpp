@@ -177,10 +177,16 @@ hipError_t launch_append_one(const PagedMap& m, const RowDesc* rows,
                              hipStream_t st);
 hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,
                       int64_t block_floats, hipStream_t st);
+// deep: two pages in flight per wave (one wave per SIMD for group 4 and 8)
+// instead of one (two waves per SIMD); the same arithmetic, so the same bits.
+// The deep form pays where waves stream long splits: a batch with 2048-key
+// splits (rows of 8192 keys and more) -- M=64 rows of 1K-16K keys 0.48 vs
+// 0.53 ms, M=256 1.657 vs 1.670 ms; without them the plain form is faster
+// (M=32 / 64 / 128 rows of 512-4096 keys: 4-6%).
 hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,
-                              int32_t group, hipStream_t st);
+                              int32_t group, bool deep, hipStream_t st);
 hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
-                              int32_t group, hipStream_t st);
+                              int32_t group, bool deep, hipStream_t st);
 // Split multi-query decode (n_q x group <= kVerifyMaxRows), then launch_merge.
 hipError_t launch_verify_mfma(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st);

@@ -303,8 +303,10 @@ __device__ __forceinline__ void merge_head(const AttnArgs& a, int32_t row,
 }
 
 // One wave's work: work item item_idx (a (row, split) pair), kv head kvh;
-// lane = this thread's lane in its wave.
-template <int GROUP, class Map>
+// lane = this thread's lane in its wave.  DEEP: two pages in flight ahead of
+// the one being used instead of one (more registers: one wave per SIMD for
+// group 4 and 8); the arithmetic is the same, page by page, so are the bits.
+template <int GROUP, class Map, bool DEEP = false>
 __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
                                             int32_t item_idx, int32_t kvh,
                                             int lane) {
@@ -394,18 +396,16 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
     }
   };
 
-  load_page(p_begin, kA, kB, vA, vB);
-  for (int32_t p = p_begin; p < p_end; ++p) {
-    float4 nkA[NI], nkB[NI], nvA[NI], nvB[NI];
-    if (p + 1 < p_end) load_page(p + 1, nkA, nkB, nvA, nvB);
-
+  // scores, online softmax and weighted sum of one page (in registers)
+  auto use_page = [&](int32_t p, const float4(&ka)[NI], const float4(&kb)[NI],
+                      const float4(&va)[NI], const float4(&vb)[NI]) {
     const int32_t n_valid = min(B, k_end - p * B);
     float s[NI][GROUP];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
 #pragma unroll
       for (int j = 0; j < GROUP; ++j)
-        s[i][j] = row16_sum(dot8(kA[i], kB[i], qa[j], qb[j]));
+        s[i][j] = row16_sum(dot8(ka[i], kb[i], qa[j], qb[j]));
     }
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -439,14 +439,14 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        xa[0] = fmaf(pr[i], vA[i].x, xa[0]);
-        xa[1] = fmaf(pr[i], vA[i].y, xa[1]);
-        xa[2] = fmaf(pr[i], vA[i].z, xa[2]);
-        xa[3] = fmaf(pr[i], vA[i].w, xa[3]);
-        xb[0] = fmaf(pr[i], vB[i].x, xb[0]);
-        xb[1] = fmaf(pr[i], vB[i].y, xb[1]);
-        xb[2] = fmaf(pr[i], vB[i].z, xb[2]);
-        xb[3] = fmaf(pr[i], vB[i].w, xb[3]);
+        xa[0] = fmaf(pr[i], va[i].x, xa[0]);
+        xa[1] = fmaf(pr[i], va[i].y, xa[1]);
+        xa[2] = fmaf(pr[i], va[i].z, xa[2]);
+        xa[3] = fmaf(pr[i], va[i].w, xa[3]);
+        xb[0] = fmaf(pr[i], vb[i].x, xb[0]);
+        xb[1] = fmaf(pr[i], vb[i].y, xb[1]);
+        xb[2] = fmaf(pr[i], vb[i].z, xb[2]);
+        xb[3] = fmaf(pr[i], vb[i].w, xb[3]);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -455,13 +455,38 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
       }
     }
 
-    if (p + 1 < p_end) {
+  };
+
+  load_page(p_begin, kA, kB, vA, vB);
+  if constexpr (DEEP) {
+    // three register pages used in turn: page p + 2 is requested while page
+    // p is used
+    float4 k1A[NI], k1B[NI], v1A[NI], v1B[NI];
+    float4 k2A[NI], k2B[NI], v2A[NI], v2B[NI];
+    if (p_begin + 1 < p_end) load_page(p_begin + 1, k1A, k1B, v1A, v1B);
+    for (int32_t p = p_begin; p < p_end; p += 3) {
+      if (p + 2 < p_end) load_page(p + 2, k2A, k2B, v2A, v2B);
+      use_page(p, kA, kB, vA, vB);
+      if (p + 1 >= p_end) break;
+      if (p + 3 < p_end) load_page(p + 3, kA, kB, vA, vB);
+      use_page(p + 1, k1A, k1B, v1A, v1B);
+      if (p + 2 >= p_end) break;
+      if (p + 4 < p_end) load_page(p + 4, k1A, k1B, v1A, v1B);
+      use_page(p + 2, k2A, k2B, v2A, v2B);
+    }
+  } else {
+    for (int32_t p = p_begin; p < p_end; ++p) {
+      float4 nkA[NI], nkB[NI], nvA[NI], nvB[NI];
+      if (p + 1 < p_end) load_page(p + 1, nkA, nkB, nvA, nvB);
+      use_page(p, kA, kB, vA, vB);
+      if (p + 1 < p_end) {
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        kA[i] = nkA[i];
-        kB[i] = nkB[i];
-        vA[i] = nvA[i];
-        vB[i] = nvB[i];
+        for (int i = 0; i < NI; ++i) {
+          kA[i] = nkA[i];
+          kB[i] = nkB[i];
+          vA[i] = nvA[i];
+          vB[i] = nvB[i];
+        }
       }
     }
   }
@@ -528,10 +553,11 @@ __device__ __forceinline__ void decode_wave(const Map& m, const AttnArgs& a,
   }
 }
 
-template <int GROUP, class Map>
+template <int GROUP, class Map, bool DEEP>
 __global__ __launch_bounds__(64) void decode_fast_kernel(Map m, AttnArgs a) {
   const int32_t item_idx = blockIdx.x / a.n_kv_heads;
-  decode_wave<GROUP>(m, a, item_idx, blockIdx.x - item_idx * a.n_kv_heads, threadIdx.x);
+  decode_wave<GROUP, Map, DEEP>(m, a, item_idx, blockIdx.x - item_idx * a.n_kv_heads,
+                                threadIdx.x);
 }
 
 // Split merge kernel: one wave per (row, query, query head) of a row with
@@ -1342,15 +1368,23 @@ hipError_t append_impl(const Map& m, const RowDesc* rows, const float* K,
   return hipGetLastError();
 }
 
-template <class Map>
-hipError_t decode_fast_impl(const Map& m, const AttnArgs& a, int32_t group,
-                            hipStream_t st) {
+template <int GROUP, class Map>
+void decode_fast_launch(const Map& m, const AttnArgs& a, bool deep, hipStream_t st) {
   const dim3 grid(a.n_items * a.n_kv_heads);
+  if (deep)
+    decode_fast_kernel<GROUP, Map, true><<<grid, 64, 0, st>>>(m, a);
+  else
+    decode_fast_kernel<GROUP, Map, false><<<grid, 64, 0, st>>>(m, a);
+}
+
+template <class Map>
+hipError_t decode_fast_impl(const Map& m, const AttnArgs& a, int32_t group, bool deep,
+                            hipStream_t st) {
   switch (group) {
-    case 1: decode_fast_kernel<1, Map><<<grid, 64, 0, st>>>(m, a); break;
-    case 2: decode_fast_kernel<2, Map><<<grid, 64, 0, st>>>(m, a); break;
-    case 4: decode_fast_kernel<4, Map><<<grid, 64, 0, st>>>(m, a); break;
-    case 8: decode_fast_kernel<8, Map><<<grid, 64, 0, st>>>(m, a); break;
+    case 1: decode_fast_launch<1>(m, a, deep, st); break;
+    case 2: decode_fast_launch<2>(m, a, deep, st); break;
+    case 4: decode_fast_launch<4>(m, a, deep, st); break;
+    case 8: decode_fast_launch<8>(m, a, deep, st); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1466,12 +1500,12 @@ hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,
 }
 
 hipError_t launch_decode_fast(const PagedMap& m, const AttnArgs& a,
-                              int32_t group, hipStream_t st) {
-  return decode_fast_impl(m, a, group, st);
+                              int32_t group, bool deep, hipStream_t st) {
+  return decode_fast_impl(m, a, group, deep, st);
 }
 hipError_t launch_decode_fast(const ContigMap& m, const AttnArgs& a,
-                              int32_t group, hipStream_t st) {
-  return decode_fast_impl(m, a, group, st);
+                              int32_t group, bool deep, hipStream_t st) {
+  return decode_fast_impl(m, a, group, deep, st);
 }
 hipError_t launch_verify_mfma(const PagedMap& m, const AttnArgs& a,
                               int32_t group, hipStream_t st) {

@@ -5,6 +5,8 @@ float32 attention outputs within 1e-4 + 1e-4 * |oracle|; paged and
 contiguous forms of the same kernel bit-identical on the GPU; outputs
 independent (bitwise) of batch composition and block placement.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -197,6 +199,42 @@ def test_decode_batch_and_placement_invariance():
     out2 = decode_step(pool2, seqs2, q, k, v, H, G, D, wl.scale, advance=False)
     assert not np.array_equal(pool.seq_pages(seqs[0]), pool2.seq_pages(seqs2[0]))
     assert bits_equal(out2, full)
+
+
+def test_decode_same_bits_in_both_launch_forms():
+    """A batch holding a row of 8192 keys or more (2048-key splits) runs the
+    decode kernel's deep form (two pages in flight per wave), a batch
+    without one the plain form: a short row gives the same bits either way
+    (same arithmetic, page by page), and matches the oracle."""
+    H, G, D = 32, 8, 128
+    rng = np.random.default_rng(2024)
+    lens = [int(x) for x in rng.integers(700, 3000, size=40)] + [9000, 12001]
+    hist = [(rng.standard_normal((l, G * D)).astype(np.float32),
+             rng.standard_normal((l, G * D)).astype(np.float32)) for l in lens]
+    n_blocks = sum(l // 16 + 2 for l in lens) + 8
+    pool = pkv.Pool(n_blocks, 16, 1, G, D, max_seqs=64)
+    pool.set_free_order(rng.permutation(n_blocks))
+    seqs = [pool.seq_new(l + 4) for l in lens]
+    fill_history(pool, seqs, lambda r: hist[r])
+    M = len(lens)
+    q = rng.standard_normal((M, H * D)).astype(np.float32)
+    k = rng.standard_normal((M, G * D)).astype(np.float32)
+    v = rng.standard_normal((M, G * D)).astype(np.float32)
+    scale = float(np.float32(1 / math.sqrt(D)))
+    full = decode_step(pool, seqs, q, k, v, H, G, D, scale, advance=False)  # deep
+    for r in (0, 1, 20, M - 1):
+        nb = pool.decode_workspace_bytes([seqs[r]], H)
+        ws = torch.empty(max(nb, 4), dtype=torch.uint8, device="cuda")
+        o1 = torch.empty((1, H * D), device="cuda")
+        pool.attn_paged_decode([seqs[r]], 0, H, G, D, dev(q[r:r + 1]), scale, o1, ws=ws,
+                               check=True)  # plain for the short rows
+        torch.cuda.synchronize()
+        assert bits_equal(o1[0], full[r]), r
+        rc, ref = oracle.attn_contig(q[r:r + 1], np.concatenate([hist[r][0], k[r:r + 1]]),
+                                     np.concatenate([hist[r][1], v[r:r + 1]]), H, G, D,
+                                     True, scale)
+        assert rc == 0
+        assert_close(o1.cpu().numpy(), ref, "row %d" % r)
 
 
 @pytest.mark.parametrize("ctx", [0, 1, 15, 16, 17, 255, 256, 511, 512, 513, 1023, 1535,
