@@ -1,7 +1,9 @@
 """Seeded randomised GPU parity: shapes (fast and generic paths), batch
-sizes, history lengths, query counts, entry points (decode, shared-prefix
-decode, verify, prefill causal / non-causal), rotary embedding on / off and
-block placement are drawn per case; every output row is compared with the
+sizes, history lengths (now and then a row of 8192+ keys, which takes the
+decode kernel's deep form), query counts, entry points (decode, the
+append-then-attend call, shared-prefix decode, verify, prefill causal /
+non-causal), rotary embedding on / off and block placement are drawn per
+case; every output row is compared with the
 oracle at 1e-4 + 1e-4 * |oracle|, and the contiguous twin must agree bit for
 bit where it applies."""
 import math
@@ -20,7 +22,7 @@ SHAPES = [  # (H, G, D, B)
     (32, 8, 128, 16), (8, 8, 128, 16), (16, 8, 128, 16), (64, 8, 128, 16),
     (12, 4, 64, 16), (6, 2, 42, 5), (32, 8, 128, 8), (4, 1, 32, 4),
 ]
-KINDS = ["decode", "shared", "verify", "prefill", "prefill_nc"]
+KINDS = ["decode", "with", "shared", "verify", "prefill", "prefill_nc"]
 LB = math.log(10000.0)
 
 
@@ -29,10 +31,12 @@ def _case(seed):
     H, G, D, B = SHAPES[rng.integers(len(SHAPES))]
     kind = KINDS[rng.integers(len(KINDS))]
     M = int(rng.integers(1, 6))
-    n_q = {"decode": 1, "shared": 1, "verify": int(rng.integers(1, 9)),
+    n_q = {"decode": 1, "with": 1, "shared": 1, "verify": int(rng.integers(1, 9)),
            "prefill": int(rng.integers(1, 70)), "prefill_nc": int(rng.integers(1, 70))}[kind]
     rope = bool(rng.integers(2)) and D % 2 == 0
     lens = [int(x) for x in rng.integers(0, 1300, size=M)]
+    if kind in ("decode", "with", "verify") and rng.random() < 0.2:
+        lens[int(rng.integers(M))] = int(rng.integers(8192, 9200))
     return rng, H, G, D, B, kind, M, n_q, rope, lens
 
 
@@ -44,7 +48,7 @@ def _turn(x, heads, D, pos, rope):
     return y
 
 
-@pytest.mark.parametrize("seed", range(120))
+@pytest.mark.parametrize("seed", range(180))
 def test_random_case(seed):
     rng, H, G, D, B, kind, M, n_q, rope, lens = _case(1000 + seed)
     scale = float(np.float32(1 / math.sqrt(D)))
@@ -81,10 +85,16 @@ def test_random_case(seed):
     K = rng.standard_normal((M * n_q, G * D), dtype=np.float32)
     V = rng.standard_normal((M * n_q, G * D), dtype=np.float32)
     pool.ensure_append(seqs, n_q, check=True)
-    pool.append_layer(seqs, n_q, 0, dev(K), dev(V), check=True)
+    if kind != "with":
+        pool.append_layer(seqs, n_q, 0, dev(K), dev(V), check=True)
     out = torch.full((M * n_q, H * D), float("nan"), device="cuda")
     causal = kind != "prefill_nc"
-    if kind == "decode":
+    if kind == "with":
+        nb = pool.decode_workspace_bytes(seqs, H)
+        ws = torch.empty(max(nb, 4), dtype=torch.uint8, device="cuda")
+        pool.attn_with_paged_decode(seqs, 0, H, G, D, dev(Q), dev(K), dev(V), scale, out,
+                                    ws=ws, check=True)
+    elif kind == "decode":
         nb = pool.decode_workspace_bytes(seqs, H)
         ws = torch.empty(max(nb, 4), dtype=torch.uint8, device="cuda")
         pool.attn_paged_decode(seqs, 0, H, G, D, dev(Q), scale, out, ws=ws, check=True)
@@ -114,12 +124,12 @@ def test_random_case(seed):
         rc, ref = oracle.attn_contig(Qr, Kc, Vc, H, G, D, causal, scale)
         assert rc == 0
         assert_close(got[rows], ref, "%s row %d (len %d)" % (what, r, L))
-    if kind in ("decode", "prefill", "prefill_nc"):
+    if kind in ("decode", "with", "prefill", "prefill_nc"):
         cc = pkv.ContigCache(M, 1, G, max(lens) + n_q, D, block_size=B, rope=table)
         fill_contig(cc, list(range(M)), lambda r: hist[r])
         cc.append(list(range(M)), lens, n_q, 0, dev(K), dev(V))
         cout = torch.full_like(out, float("nan"))
-        if kind == "decode":
+        if kind in ("decode", "with"):
             cws = torch.empty(max(cc.decode_workspace_bytes(lens, H), 4), dtype=torch.uint8,
                               device="cuda")
             cc.attn_decode(list(range(M)), lens, 0, H, dev(Q), scale, cout, ws=cws)
