@@ -214,11 +214,15 @@ def bench_decode(args, synth, pkv):
         """warmup + timed steps from step index t_first (rows cached before
         step t: ctx + t); the library times the launches of `kernels` (ids,
         None: all) with HIP events on its stream."""
+        # warm-up steps carry the timing events too: the first timed launches
+        # of a process have stalled the host once for ~35 ms (HIP runtime
+        # set-up), which must not land in the timed steps
+        pool.profile_kernels(kernels)
+        pool.profile_enable(True)
         for t in range(t_first, t_first + args.warmup):
             step(t)
         torch.cuda.synchronize()
-        pool.profile_kernels(kernels)
-        pool.profile_enable(True)
+        pool.profile_enable(True)  # clears the warm-up's totals
         # per-step GPU time: events on the stream the library is given
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
         torch.cuda.synchronize()
@@ -355,6 +359,7 @@ def bench_verify(args, wl, pool, seqs, n_q, pkv, torch):
             lens[r] += int(accept[t, r])
 
     lens = [pool.seq_len(s) for s in seqs]
+    pool.profile_enable(True)  # warm-up with the timing events on (see run())
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
@@ -433,6 +438,7 @@ def bench_forked(args, synth, pkv, shared):
         pool.advance(seqs_np, 1, check=True)
 
     w = min(args.warmup, wl.steps - 1)
+    pool.profile_enable(True)  # warm-up with the timing events on (see run())
     for t in range(w):
         step(t)
     torch.cuda.synchronize()
@@ -594,10 +600,11 @@ def bench_decode_small(args, synth, pkv):
         pool.attn_paged_decode(seqs_np, 0, H, G, D, q, wl.scale, out, ws=ws, check=True)
         pool.advance(seqs_np, 1, check=True)
 
+    pool.profile_kernels([pkv.K_DECODE])
+    pool.profile_enable(True)  # warm-up with the timing events on (see run())
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
-    pool.profile_kernels([pkv.K_DECODE])
     pool.profile_enable(True)
     t0 = time.perf_counter()
     for t in range(args.warmup, n_steps):
@@ -649,6 +656,7 @@ def bench_prefill(args, synth, pkv):
         for s in seqs:  # rewind so the next step appends the same chunk
             pool.seq_truncate(s, wl.cached, check=True)
 
+    pool.profile_enable(True)  # warm-up with the timing events on (see run())
     for _ in range(2):
         step()
     torch.cuda.synchronize()

@@ -453,7 +453,11 @@ int32_t pkv_pool_free_stack(pkv_pool *pool, int64_t *out, int32_t cap);
 #define PKV_K_COUNT 7
 
 /* on != 0: record a HIP event pair on the launch stream around every kernel
- * the pool launches; on == 0: stop.  Either way, clears the totals. */
+ * the pool launches; on == 0: stop.  Either way, clears the totals (after
+ * waiting for the pool's stream).  Switching on makes the events for the
+ * next 128 timed launches up front (creating a HIP event can take the host
+ * hundreds of microseconds, which would otherwise land inside timed steps);
+ * events are reused by later profiling runs. */
 int32_t pkv_profile_enable(pkv_pool *pool, int32_t on);
 
 /* Which kernels profiling times: bit k of mask selects kernel id k (all by

@@ -36,6 +36,8 @@ using pkv::RowDesc;
 
 constexpr double kLog2e = 1.4426950408889634074;
 constexpr int kStageSlots = 8;
+// Timing events made when profiling is switched on (two per timed launch).
+constexpr size_t kProfReserve = 256;
 
 enum Buf { kRows = 0, kCow = 1, kNumBufs = 2 };
 
@@ -102,6 +104,20 @@ struct DeviceCtx {
       }
       v.clear();
     }
+  }
+
+  // Timing events for the next profiled launches, made before they are
+  // needed: creating one can cost the host hundreds of microseconds.
+  hipError_t reserve_events(size_t n, hipStream_t st) {
+    const size_t had = ev_pool.size();
+    while (ev_pool.size() < n) {
+      hipEvent_t e = nullptr;
+      hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) return r;
+      ev_pool.push_back(e);
+      if ((r = hipEventRecord(e, st)) != hipSuccess) return r;
+    }
+    return ev_pool.size() > had ? hipStreamSynchronize(st) : hipSuccess;
   }
 
   hipEvent_t take_event() {
@@ -1234,6 +1250,9 @@ int32_t pkv_profile_enable(pkv_pool* pool, int32_t on) {
     return PKV_ERR_DEVICE;
   pool->dev.clear_prof();
   pool->dev.prof_on = on != 0;
+  if (on && pool->storage &&
+      pool->dev.reserve_events(kProfReserve, pool->dev.last_stream) != hipSuccess)
+    return PKV_ERR_DEVICE;
   return PKV_OK;
 }
 
