@@ -1,7 +1,8 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times: sampled outputs against the oracle (one sequence / query at
 a time), properties on every output, pool state against the oracle's, and
-the fork / rewind invariants bit for bit."""
+the fork / rewind invariants bit for bit.  Decode, verify (4 and 8 drafted
+rows with rewind), prefill and the forked workload."""
 import numpy as np
 import pytest
 import torch
@@ -53,6 +54,58 @@ def test_decode_m256_full_size_sampled_rows():
         assert rc == 0
         assert_close(got[r:r + 1], ref, "m256 row %d (ctx %d)" % (r, wl.ctx[r]))
     pool.advance(seqs_np, 1, check=True)
+    pool.close()
+
+
+def test_verify_m256_full_size_sampled_rows_with_rewind():
+    """The verify legs' launches: every sequence of the M=256 pool appends 4
+    drafted rows and attends them offset-causally, keeps a seeded 1..4 of
+    them (truncate), then appends and attends 8 more.  Sampled rows against
+    the oracle over the history plus the kept rows, at both steps."""
+    wl = synth.decode_m256(max_steps=16)
+    H, G, D, M = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.M
+    pool = _pool_for(wl)
+    seqs = [pool.seq_new(wl.max_tokens) for _ in range(M)]
+    f = HistoryFiller(wl, int(wl.ctx.max()))
+    f.fill(pool, seqs, wl.ctx)
+    f.close()
+    seqs_np = np.asarray(seqs, np.int32)
+    gen = np.random.default_rng(41)
+    kept = [np.zeros((0, G * D), np.float32) for _ in range(M)]
+    kept_v = [np.zeros((0, G * D), np.float32) for _ in range(M)]
+    rows = sorted({int(np.argmin(wl.ctx)), int(np.argmax(wl.ctx)), 0, 1, 77, 128, 255})
+    for n_q in (4, 8):
+        q = gen.standard_normal((M * n_q, H * D), dtype=np.float32)
+        k = gen.standard_normal((M * n_q, G * D), dtype=np.float32)
+        v = gen.standard_normal((M * n_q, G * D), dtype=np.float32)
+        pool.ensure_append(seqs_np, n_q, check=True)
+        pool.append_layer(seqs_np, n_q, 0, dev(k), dev(v), check=True)
+        nb = pool.verify_workspace_bytes(seqs_np, n_q, H)
+        ws = torch.empty(max(nb, 4), dtype=torch.uint8, device="cuda")
+        out = torch.full((M * n_q, H * D), float("nan"), device="cuda")
+        pool.attn_paged_verify(seqs_np, n_q, 0, H, G, D, dev(q), wl.scale, out, ws=ws,
+                               check=True)
+        pool.advance(seqs_np, n_q, check=True)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.all(np.isfinite(got))
+        assert np.abs(got).max() < 10
+        for r in rows:
+            kh, vh = wl.history(r)
+            sl = slice(r * n_q, (r + 1) * n_q)
+            rc, ref = oracle.attn_contig(q[sl], np.concatenate([kh, kept[r], k[sl]]),
+                                         np.concatenate([vh, kept_v[r], v[sl]]), H, G, D,
+                                         True, wl.scale)
+            assert rc == 0
+            assert_close(got[sl], ref, "verify n_q %d row %d (ctx %d)" % (n_q, r, wl.ctx[r]))
+        # keep a seeded 1..n_q of the drafted rows, rewind the rest
+        accept = gen.integers(1, n_q + 1, size=M)
+        for r, s in enumerate(seqs):
+            new_len = int(wl.ctx[r]) + kept[r].shape[0] + int(accept[r])
+            pool.seq_truncate(s, new_len, check=True)
+            assert pool.seq_len(s) == new_len
+            kept[r] = np.concatenate([kept[r], k[r * n_q:r * n_q + int(accept[r])]])
+            kept_v[r] = np.concatenate([kept_v[r], v[r * n_q:r * n_q + int(accept[r])]])
     pool.close()
 
 
