@@ -1,5 +1,6 @@
 """Host-side helpers of bench.py (no GPU)."""
 import os
+import subprocess
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -23,3 +24,13 @@ def test_code_digest_ignores_comments_only(tmp_path):
 def test_percentiles():
     p = bench.pct([1.0, 2.0, 3.0, 4.0, 5.0])
     assert p["p50"] == 3.0 and p["p10"] < p["p50"] < p["p90"]
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    for argv, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + argv,
+                           env=dict(os.environ, **env), capture_output=True, text=True,
+                           timeout=120)
+        assert r.returncode == 2
+        assert "one GPU only" in r.stderr
+        assert r.stdout == ""
