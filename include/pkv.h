@@ -98,8 +98,12 @@ size_t pkv_pool_storage_bytes(int32_t n_blocks, int32_t block_size,
  * pkv_pool_free.  storage_dev == NULL makes a metadata-only pool: every
  * block, sequence and page-table call works and no device work is ever
  * done; pkv_append_layer runs its checks and then does nothing, and the
- * attention calls return PKV_ERR_BAD_ARG.  max_seqs bounds the
- * number of live sequence ids.  Returns NULL on bad sizes or a HIP failure.
+ * attention calls return PKV_ERR_BAD_ARG.  max_seqs bounds the number of
+ * live sequence ids; the device page-table mirror gives each id at least 64
+ * int32-addressed entries, so max_seqs * 64 must not exceed 2^31 - 1.
+ * Makes no HIP call.  Returns NULL on a size <= 0, max_seqs too large,
+ * storage_bytes below pkv_pool_storage_bytes, storage_dev not 256-byte
+ * aligned, or host memory exhausted.
  * A fresh pool hands out block ids 0, 1, 2, ... in that order. */
 pkv_pool *pkv_pool_new(int32_t n_blocks, int32_t block_size, int32_t n_layers,
                        int32_t n_kv_heads, int32_t head_dim, int32_t max_seqs,
@@ -114,15 +118,20 @@ void pkv_pool_free(pkv_pool *pool);
  * a released id is handed out again.) */
 int64_t pkv_alloc_block(pkv_pool *pool);
 
-/* Drop one reference; at zero the id returns to the free stack, from which
- * the most recently released id is taken first.  PKV_ERR_BAD_ARG for an id
- * out of range or already free. */
+/* Give back a reference taken by pkv_alloc_block; at zero the id returns to
+ * the free stack, from which the most recently released id is taken first
+ * ("nx_paged_kv_gate.nx source", KAT part: a released id is handed out
+ * again).  Only such references can be dropped here: a block's count minus
+ * the page-table entries that name it (those are released by
+ * pkv_seq_truncate and pkv_seq_free).  PKV_ERR_BAD_ARG, with nothing
+ * changed, for an id out of range, a free id, or a block whose remaining
+ * references all belong to page tables. */
 int32_t pkv_unref_block(pkv_pool *pool, int64_t id);
 
 /* Placement control: afterwards, allocations return ids[0], ids[1], ... in
  * that order.  ids[0..n) must be a permutation of exactly the currently free
- * ids (PKV_ERR_BAD_ARG otherwise).  Used to scatter sequences across the
- * pool with a seeded permutation. */
+ * ids (PKV_ERR_BAD_ARG, with nothing changed, otherwise).  Used to scatter
+ * sequences' pages across the pool with a seeded permutation. */
 int32_t pkv_pool_set_free_order(pkv_pool *pool, const int64_t *ids,
                                 int32_t n);
 
@@ -166,7 +175,11 @@ int32_t pkv_pool_set_rope(pkv_pool *pool, const pkv_rope *rope);
 
 /* New empty sequence that may hold up to max_tokens rows; returns the lowest
  * unused id, -PKV_ERR_BAD_ARG for max_tokens <= 0, -PKV_ERR_CAPACITY when
- * max_seqs ids are live.  ("nx_paged_kv_gate.nx source": nx_pkv_seq_new.) */
+ * max_seqs ids are live or when the device page-table mirror could not
+ * address the new page table with int32 offsets: max_seqs times the longest
+ * page table of any sequence (ceil(max_tokens / block_size), rounded up to a
+ * multiple of 64) must not exceed 2^31 - 1.  Nothing changes on an error.
+ * ("nx_paged_kv_gate.nx source": nx_pkv_seq_new.) */
 int32_t pkv_seq_new(pkv_pool *pool, int32_t max_tokens);
 
 /* Release every page of the sequence (last page first) and retire its id. */

@@ -404,15 +404,43 @@ int64_t pkvo_alloc_block(OPool *p)
 }
 
 /* Drop one reference; at zero the id goes back on the free stack. */
+static void drop_ref(OPool *p, int64_t id)
+{
+    p->refcnt[id] -= 1;
+    if (p->refcnt[id] == 0)
+        p->free_stack[p->n_free++] = id;
+}
+
+/* Number of page-table entries, over all live sequences, that name id. */
+static int page_table_holders(const OPool *p, int64_t id)
+{
+    int n = 0;
+    for (int s = 0; s < p->max_seqs; s++) {
+        const OSeq *q = &p->seqs[s];
+        if (!q->alive)
+            continue;
+        for (int pg = 0; pg < q->n_pages; pg++)
+            if (q->pt[pg] == id)
+                n++;
+    }
+    return n;
+}
+
+/*
+ * [P4] KAT part: a block handed out by alloc_block is given back with
+ * unref_block and its id is recycled.  Reading: unref_block releases only
+ * such references -- the block's count minus the page-table entries that
+ * name it; those are released by truncate and free.  Anything else (an id
+ * out of range, a free id, a block whose remaining references are all page
+ * table entries) is refused with BAD_ARG and changes nothing.
+ */
 int pkvo_unref_block(OPool *p, int64_t id)
 {
     if (id < 0 || id >= p->n_blocks)
         return O_BAD_ARG;
-    if (p->refcnt[id] <= 0)
+    if (p->refcnt[id] - page_table_holders(p, id) <= 0)
         return O_BAD_ARG;
-    p->refcnt[id] -= 1;
-    if (p->refcnt[id] == 0)
-        p->free_stack[p->n_free++] = id;
+    drop_ref(p, id);
     return O_OK;
 }
 
@@ -477,7 +505,7 @@ int pkvo_seq_new(OPool *p, int max_tokens)
 static void release_tail(OPool *p, OSeq *q, int keep)
 {
     for (int pg = q->n_pages - 1; pg >= keep; pg--)
-        pkvo_unref_block(p, q->pt[pg]);
+        drop_ref(p, q->pt[pg]);
     if (q->n_pages > keep)
         q->n_pages = keep;
 }

@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <functional>
@@ -449,13 +450,12 @@ namespace {
 // a new mirror is filled from every live page-table entry.
 hipError_t size_mirror(pkv_pool* p, hipStream_t st) {
   auto& m = p->meta;
-  const int64_t need = std::max<int64_t>(m.max_pages_seen(), 1);
-  if (p->mirror && need <= p->stride) return hipSuccess;
+  const int64_t stride = pkv::PoolMeta::mirror_stride(m.max_pages_seen());
+  if (p->mirror && stride <= p->stride) return hipSuccess;
   hipError_t e;
   if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
   if (p->mirror) (void)hipFree(p->mirror);
   p->mirror = nullptr;
-  const int64_t stride = (need + 63) / 64 * 64;
   if ((e = hipMalloc(&p->mirror, static_cast<size_t>(m.max_seqs()) * stride *
                                      sizeof(int32_t))) != hipSuccess)
     return e;
@@ -729,9 +729,12 @@ pkv_pool* pkv_pool_new(int32_t n_blocks, int32_t block_size, int32_t n_layers,
   const size_t need = pkv_pool_storage_bytes(n_blocks, block_size, n_layers,
                                              n_kv_heads, head_dim);
   if (need == 0 || max_seqs <= 0) return nullptr;
+  // the page-table mirror holds at least 64 int32-addressed entries per id
+  if (static_cast<int64_t>(max_seqs) * pkv::PoolMeta::mirror_stride(1) > INT32_MAX)
+    return nullptr;
   if (storage_dev) {
     if (storage_bytes < need) return nullptr;
-    if (reinterpret_cast<uintptr_t>(storage_dev) % 16 != 0) return nullptr;
+    if (reinterpret_cast<uintptr_t>(storage_dev) % 256 != 0) return nullptr;
   }
   pkv_pool* p = new (std::nothrow) pkv_pool(n_blocks, block_size, n_layers,
                                             n_kv_heads, head_dim, max_seqs);

@@ -2,6 +2,7 @@
 #include "pool_meta.hpp"
 
 #include <algorithm>
+#include <climits>
 #include <unordered_map>
 
 namespace pkv {
@@ -19,6 +20,7 @@ PoolMeta::PoolMeta(int32_t n_blocks, int32_t block_size, int32_t n_layers,
       head_dim_(head_dim),
       max_seqs_(max_seqs),
       refcnt_(n_blocks, 0),
+      held_(n_blocks, 0),
       free_(n_blocks),
       seqs_(max_seqs),
       stamp_(max_seqs, 0) {
@@ -34,17 +36,20 @@ int32_t PoolMeta::pop() {
 }
 
 void PoolMeta::drop_ref(int32_t b) {
-  // A count already at zero (the caller released a block a sequence still
-  // names) is left alone rather than driven negative.
-  if (refcnt_[b] > 0 && --refcnt_[b] == 0) free_.push_back(b);
+  // never below the page-table holders: unref_block refuses their references
+  if (--refcnt_[b] == 0) free_.push_back(b);
 }
 
-// Every page-table write goes through here so the device mirror can follow.
+// Every page-table write goes through here so the device mirror and the
+// holder counts can follow.
 void PoolMeta::set_page(int32_t s, SeqMeta& q, int32_t p, int32_t block) {
-  if (p == static_cast<int32_t>(q.pages.size()))
+  if (p == static_cast<int32_t>(q.pages.size())) {
     q.pages.push_back(block);
-  else
+  } else {
+    --held_[q.pages[p]];
     q.pages[p] = block;
+  }
+  ++held_[block];
   if (track_) patches_.push_back({s, p, block});
 }
 
@@ -56,7 +61,9 @@ int64_t PoolMeta::alloc_block() {
 
 int32_t PoolMeta::unref_block(int64_t id) {
   if (id < 0 || id >= n_blocks_) return kBadArg;
-  if (refcnt_[id] <= 0) return kBadArg;
+  // only references taken by alloc_block: the page-table entries naming the
+  // block are released by truncate and free
+  if (refcnt_[id] - held_[id] <= 0) return kBadArg;
   ++version_;
   drop_ref(static_cast<int32_t>(id));
   return kOk;
@@ -96,6 +103,10 @@ int32_t PoolMeta::seq_new(int32_t max_tokens) {
   if (max_tokens <= 0) return -kBadArg;
   const int32_t s = lowest_free_id();
   if (s < 0) return -kCapacity;
+  // the device mirror addresses entry (seq, page) at seq * stride + page in
+  // int32
+  const int64_t pages = std::max(max_pages_seen_, pages_for(max_tokens, block_size_));
+  if (static_cast<int64_t>(max_seqs_) * mirror_stride(pages) > INT32_MAX) return -kCapacity;
   SeqMeta& q = seqs_[s];
   q.alive = true;
   q.seq_len = 0;
@@ -109,6 +120,7 @@ int32_t PoolMeta::seq_new(int32_t max_tokens) {
 
 void PoolMeta::release_from(SeqMeta& q, int32_t keep_pages) {
   while (static_cast<int32_t>(q.pages.size()) > keep_pages) {
+    --held_[q.pages.back()];
     drop_ref(q.pages.back());
     q.pages.pop_back();
   }

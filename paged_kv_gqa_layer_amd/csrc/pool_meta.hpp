@@ -16,9 +16,16 @@
 //     changes nothing if too few are free;
 //   - truncate and free release pages from the last page backwards;
 //   - fork shares ceil(seq_len / block_size) pages;
-//   - the lowest unused sequence id is handed out.
+//   - the lowest unused sequence id is handed out;
+//   - unref_block releases only references taken by alloc_block: a block's
+//     count minus the page-table entries that name it (those are released by
+//     truncate and free);
+//   - seq_new refuses a max_tokens whose page table, at the device mirror's
+//     stride (pages rounded up to 64), would put a sequence's mirror offset
+//     past the int32 range.
 #pragma once
 
+#include <algorithm>
 #include <cstdint>
 #include <utility>
 #include <vector>
@@ -102,6 +109,13 @@ class PoolMeta {
   std::vector<PagePatch>& patches() { return patches_; }
   // Largest page-table length any sequence created so far may reach.
   int32_t max_pages_seen() const { return max_pages_seen_; }
+  // Page-table entries (over all live sequences) that name each block.
+  const std::vector<int32_t>& holders() const { return held_; }
+  // Entries per sequence of the device page-table mirror for a longest page
+  // table of `pages` entries (a multiple of 64).
+  static int64_t mirror_stride(int64_t pages) {
+    return (std::max<int64_t>(pages, 1) + 63) / 64 * 64;
+  }
 
  private:
   SeqMeta* live(int32_t s);
@@ -113,6 +127,7 @@ class PoolMeta {
 
   int32_t n_blocks_, block_size_, n_layers_, n_kv_heads_, head_dim_, max_seqs_;
   std::vector<int32_t> refcnt_;
+  std::vector<int32_t> held_;  // page-table entries naming each block
   std::vector<int32_t> free_;  // stack; back() is taken next
   std::vector<SeqMeta> seqs_;
   mutable std::vector<uint64_t> stamp_;  // duplicate detection in batches

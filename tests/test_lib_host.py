@@ -43,6 +43,64 @@ def test_pool_new_rejects_bad_sizes():
     L = pkv.lib()
     assert not L.pkv_pool_new(0, 4, 1, 1, 4, 4, None, 0)
     assert not L.pkv_pool_new(4, 4, 1, 1, 4, 0, None, 0)
+    # 64 mirror entries per sequence id must stay int32-addressable
+    assert not L.pkv_pool_new(4, 4, 1, 1, 4, (1 << 25), None, 0)
+    h = L.pkv_pool_new(4, 4, 1, 1, 4, (1 << 25) - 1, None, 0)
+    assert h
+    L.pkv_pool_free(h)
+
+
+def test_pool_new_checks_storage_size_and_alignment():
+    """The pool only records the storage pointer (no HIP call), so address
+    values stand in for device memory here: 256-byte alignment and at least
+    pkv_pool_storage_bytes bytes are required."""
+    L = pkv.lib()
+    need = pkv.pool_storage_bytes(4, 4, 1, 1, 4)
+    base = 1 << 20
+    for off, nbytes, ok in ((0, need, True), (0, need - 1, False), (16, need, False),
+                            (128, need, False), (256, need, True)):
+        h = L.pkv_pool_new(4, 4, 1, 1, 4, 4, base + off, nbytes)
+        assert bool(h) == ok, (off, nbytes)
+        if h:
+            L.pkv_pool_free(h)
+
+
+def test_seq_new_refuses_page_tables_past_int32_mirror_offsets():
+    """max_seqs x (longest page table rounded up to 64 entries) must fit in
+    int32: a sequence that would break that is refused with CAPACITY and the
+    pool is left as it was."""
+    max_seqs = 32768
+    p = pkv.Pool(64, 16, 1, 8, 128, max_seqs=max_seqs, device=None)
+    a = p.seq_new(1 << 20)               # 65536 pages: 32768 * 65536 = 2^31
+    assert a == -pkv.CAPACITY
+    assert p.seq_len(0) == -pkv.ERR_SEQ  # no sequence was made
+    ok_tokens = (65536 - 64) * 16        # 65472 pages: 32768 * 65472 < 2^31
+    a = p.seq_new(ok_tokens)
+    assert a == 0
+    assert p.seq_new(1 << 20) == -pkv.CAPACITY
+    assert p.seq_new(16) == 1
+    assert p.ensure_append([a], 100) == 0 and p.advance([a], 100) == 0
+    assert p.seq_len(a) == 100
+
+
+def test_unref_refuses_page_table_references():
+    """unref_block drops only references taken by alloc_block; the library and
+    the oracle refuse the rest the same way and keep the same state."""
+    for impl in ("lib", "oracle"):
+        p = (pkv.Pool(8, 4, 1, 1, 4, device=None) if impl == "lib"
+             else oracle.Pool(8, 4, 1, 1, 4, with_storage=False))
+        a = p.seq_new(64)
+        assert p.ensure_append([a], 6) == 0 and p.advance([a], 6) == 0
+        b0 = int(p.seq_pages(a)[0])
+        f = p.seq_fork(a)
+        assert f >= 0
+        raw = int(p.alloc_block())
+        st = (p.refcounts().tolist(), p.free_stack().tolist())
+        assert p.unref_block(b0) == pkv.BAD_ARG, impl
+        assert (p.refcounts().tolist(), p.free_stack().tolist()) == st
+        assert p.unref_block(raw) == 0
+        assert p.seq_free(f) == 0 and p.seq_free(a) == 0
+        assert p.refcounts().tolist() == [0] * 8
 
 
 def test_known_answers_from_pages():
@@ -125,11 +183,15 @@ def test_random_ops_state_matches_oracle(seed):
             if b1 >= 0:
                 raw.append(b1)
         elif op == 5:
-            if raw and rng.random() < 0.8:
+            if raw and rng.random() < 0.7:
                 b = raw.pop()
-            else:  # an id that is free or out of range: both must refuse it
+            else:  # an id that is free, out of range or held by a page
+                # table (but not raw): both must refuse it
                 free = o.free_stack().tolist()
-                b = int(rng.choice(free + [-1, n_blocks]))
+                held = [int(x) for q in range(max_seqs)
+                        for x in (o.seq_pages(q) if o.seq_pages(q) is not None else [])
+                        if int(x) not in raw]
+                b = int(rng.choice(free + held + [-1, n_blocks]))
             assert o.unref_block(b) == p.unref_block(b)
         else:
             M = int(rng.integers(0, 4))

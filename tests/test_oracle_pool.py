@@ -382,3 +382,67 @@ def test_paged_attention_equals_contiguous_on_random_histories(seed):
         c = p.seq_fork(parent)
         if c >= 0:
             hist[c] = list(hist[parent])
+
+
+# ------------------------------------------- placement and block release
+
+def test_set_free_order_sets_the_allocation_order():
+    """After set_free_order(ids), allocations return ids[0], ids[1], ...,
+    then -1; sequences take their pages in that order; a list that is not a
+    permutation of exactly the free ids is refused and changes nothing."""
+    rng = np.random.default_rng(7)
+    n = 12
+    p = oracle.Pool(n, 4, 1, 1, 4, with_storage=False)
+    order = rng.permutation(n)
+    assert p.set_free_order(order) == 0
+    assert [p.alloc_block() for _ in range(n)] == order.tolist()
+    assert p.alloc_block() == -1
+
+    # with some ids taken, the order is over the free ones only
+    p = oracle.Pool(n, 4, 1, 1, 4, with_storage=False)
+    taken = [p.alloc_block() for _ in range(3)]
+    assert taken == [0, 1, 2]
+    free_now = list(range(3, n))
+    stack = p.free_stack().tolist()
+    for bad in (free_now[:-1],                      # one short
+                free_now + [0],                     # a taken id added
+                [0] + free_now[1:],                 # a taken id in place of a free one
+                free_now[:-1] + [free_now[0]],      # a repeat
+                free_now[:-1] + [n],                # out of range
+                free_now[:-1] + [-1]):
+        assert p.set_free_order(bad) == oracle.BAD_ARG
+        assert p.free_stack().tolist() == stack
+    order = [int(x) for x in rng.permutation(free_now)]
+    assert p.set_free_order(order) == 0
+    s = p.seq_new(64)
+    assert p.ensure_append([s], 9) == 0            # 3 pages of 4 rows
+    assert p.seq_pages(s).tolist() == order[:3]
+    assert [p.alloc_block() for _ in range(2)] == order[3:5]
+    # a released id is taken next (LIFO), before the rest of the order
+    assert p.unref_block(taken[1]) == 0
+    assert p.alloc_block() == taken[1]
+    assert p.alloc_block() == order[5]
+
+
+def test_unref_releases_only_alloc_references():
+    """unref_block gives back references taken by alloc_block; references
+    that page tables hold are released by truncate and free, and an unref
+    that would take one is refused with nothing changed."""
+    p = oracle.Pool(8, 4, 1, 1, 4, with_storage=False)
+    a = p.seq_new(64)
+    assert p.ensure_append([a], 6) == 0 and p.advance([a], 6) == 0
+    b0, b1 = p.seq_pages(a).tolist()
+    before = (p.refcounts().tolist(), p.free_stack().tolist())
+    assert p.unref_block(b0) == oracle.BAD_ARG
+    assert (p.refcounts().tolist(), p.free_stack().tolist()) == before
+    f = p.seq_fork(a)                               # two holders, count 2
+    assert p.refcounts()[b0] == 2
+    assert p.unref_block(b0) == oracle.BAD_ARG
+    assert p.refcounts()[b0] == 2
+    raw = p.alloc_block()
+    assert p.unref_block(raw) == 0                  # its own reference
+    assert p.unref_block(raw) == oracle.BAD_ARG     # now free
+    assert p.seq_free(f) == 0 and p.refcounts()[b0] == 1
+    assert p.seq_truncate(a, 0) == 0
+    assert p.refcounts()[b0] == 0 and p.refcounts()[b1] == 0
+    assert p.free_stack().tolist()[-2:] == [b1, b0]  # last page released first
