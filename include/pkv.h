@@ -265,6 +265,33 @@ int32_t pkv_attn_paged_decode(pkv_pool *pool, const int32_t *seqs, int32_t M,
                               const float *Q_dev, float scale, float *out_dev,
                               void *ws_dev, size_t ws_bytes, void *stream);
 
+/* pkv_attn_paged_decode for callers that cannot allocate memory during the
+ * call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same checks, kernels and results (bit for bit),
+ * but no workspace argument and no allocation of any kind -- the split
+ * partials and the batch's row descriptors live in a fixed device array
+ * built into the library (one per GPU, 1 MiB for descriptors + 64 MiB for
+ * partials, held from the first use of the library's kernels on that GPU
+ * until the process ends), and the descriptors reach it as kernel arguments
+ * (one small launch per 896 ints) instead of through a staging buffer.
+ * Every call on one GPU shares that array: calls whose device work overlaps
+ * on one GPU (other streams, other pools, other threads) race and must be
+ * serialised by the caller.  Nothing in the array needs to start at zero.
+ * Errors as pkv_attn_paged_decode (minus the workspace ones), then
+ * PKV_ERR_UNSUPPORTED if the pool's device page-table mirror would first
+ * have to grow (it is sized by the pool's first device call after a
+ * pkv_seq_new with a longer max_tokens than any before: run
+ * pkv_append_layer first, as the step protocol does), PKV_ERR_CAPACITY if
+ * the batch's descriptors or partials exceed the array's regions, and
+ * PKV_ERR_DEVICE.  Kernel timing (pkv_profile_*) covers its launches only
+ * while events made by pkv_profile_enable remain. */
+int32_t pkv_attn_paged_decode_noalloc(pkv_pool *pool, const int32_t *seqs,
+                                      int32_t M, int32_t layer,
+                                      int32_t n_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, const float *Q_dev,
+                                      float scale, float *out_dev,
+                                      void *stream);
+
 /* Append, then attend, for one new row per sequence: the pages' per-layer
  * wrapper (append this layer's K/V rows, then paged GQA attention over
  * every row including the new one) as one call.  It runs

@@ -229,6 +229,19 @@ class Pool:
             self._h, _vp(a), a.size, layer, n_heads, n_kv_heads, head_dim, qp,
             float(scale), op, wp, wb, _stream(stream)), "attn_paged_decode", check)
 
+    def attn_paged_decode_noalloc(self, seqs, layer, n_heads, n_kv_heads, head_dim,
+                                  Q, scale, out, stream=None, check=False):
+        """attn_paged_decode without a workspace and without allocating: the
+        library's fixed per-GPU device array holds the descriptors and split
+        partials (calls overlapping on one GPU race)."""
+        a = _ids(seqs)
+        q_dim = n_heads * head_dim
+        qp = _dptr(Q, "Q", a.size * q_dim)
+        op = _dptr(out, "out", a.size * q_dim)
+        return _check(lib().pkv_attn_paged_decode_noalloc(
+            self._h, _vp(a), a.size, layer, n_heads, n_kv_heads, head_dim, qp,
+            float(scale), op, _stream(stream)), "attn_paged_decode_noalloc", check)
+
     def attn_with_paged_decode(self, seqs, layer, n_heads, n_kv_heads, head_dim,
                                Q, K_new, V_new, scale, out, ws=None, stream=None,
                                check=False):

@@ -72,6 +72,8 @@ struct DeviceCtx {
 
   bool prof_on = false;
   uint32_t prof_mask = ~0u;  // kernel ids timed while prof_on
+  // while set, timing uses only events made earlier (none are created)
+  bool no_new_events = false;
   std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[PKV_K_COUNT];
   // Timing events of earlier profiling runs, reused (creating timing events
   // can cost the host more than a short step).
@@ -127,6 +129,7 @@ struct DeviceCtx {
       ev_pool.pop_back();
       return e;
     }
+    if (no_new_events) return nullptr;
     hipEvent_t e = nullptr;
     return hipEventCreate(&e) == hipSuccess ? e : nullptr;
   }
@@ -427,6 +430,7 @@ struct pkv_pool {
   int64_t stride = 0;
   // the row blob currently in dev.buf[kRows]
   std::vector<int32_t> rows;
+  std::vector<int32_t> na_rows;  // the last zero-allocation decode's blob
   RowPlan plan;
   std::vector<int64_t> rows_key;
   size_t patch_off = 0;  // patches follow the rows in the blob
@@ -472,13 +476,51 @@ hipError_t size_mirror(pkv_pool* p, hipStream_t st) {
   return hipSuccess;
 }
 
-// Row descriptors of this batch (n new rows per sequence; with
-// shared_heads > 0 -- the query heads per kv head -- grouped by shared
-// prefix) on the device, with the pending page-table patches applied to the
-// mirror first.  Rows and patches travel in one
-// upload, which is skipped when the device copy already describes this batch
-// at this pool version (no patches can be pending then: every page-table
-// change bumps the version).
+// The row blob of a batch (n new rows per sequence; with shared_heads > 0 --
+// the query heads per kv head -- grouped by shared prefix) for the mirror's
+// current stride, followed by the pending page-table patches (from int32
+// offset *patch_off on, three ints each).
+void build_blob(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
+                int32_t shared_heads, std::vector<int32_t>& blob, RowPlan* plan,
+                size_t* patch_off) {
+  const bool shared = shared_heads > 0;
+  if (shared) find_shared(p->meta, seqs, M, shared_heads, &p->shared);
+  const int32_t B = p->meta.block_size();
+  const bool grouped = shared && !p->shared.groups.empty();
+  *plan = build_rows(blob, M, n, grouped, [&](int32_t r) {
+    const pkv::SeqMeta* q = p->meta.seq(seqs[r]);
+    RowIn in;
+    in.start = q->seq_len;
+    in.pt_off = static_cast<int32_t>(seqs[r] * p->stride);
+    const size_t pg = static_cast<size_t>(q->seq_len / B);
+    in.append_block = pg < q->pages.size() ? static_cast<int32_t>(q->pages[pg]) : -1;
+    if (shared) {
+      in.k_off = p->shared.k_off[r];
+      in.n_pre = p->shared.n_pre[r];
+    }
+    return in;
+  });
+  if (shared) append_shared(blob, p->shared, plan);
+  // The patch kernel writes entries in parallel, so keep only the last
+  // write of each (sequence, page) entry (a fork's share followed by a
+  // copy-on-append replacement, for example).
+  *patch_off = blob.size();
+  p->seen.clear();
+  const auto& pt = p->meta.patches();
+  for (auto it = pt.rbegin(); it != pt.rend(); ++it) {
+    if (!p->seen.insert(static_cast<int64_t>(it->seq) * p->stride + it->page).second)
+      continue;
+    blob.push_back(it->seq);
+    blob.push_back(it->page);
+    blob.push_back(it->block);
+  }
+}
+
+// Row descriptors of this batch (see build_blob) on the device, with the
+// pending page-table patches applied to the mirror first.  Rows and patches
+// travel in one upload, which is skipped when the device copy already
+// describes this batch at this pool version (no patches can be pending then:
+// every page-table change bumps the version).
 hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
                      int32_t shared_heads, hipStream_t st, const int32_t** rows_dev,
                      pkv::PatchArgs* deferred = nullptr) {
@@ -493,36 +535,7 @@ hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
   key.insert(key.end(), seqs, seqs + M);
   auto& pt = p->meta.patches();
   if (key != p->rows_key || !pt.empty()) {
-    const bool shared = shared_heads > 0;
-    if (shared) find_shared(p->meta, seqs, M, shared_heads, &p->shared);
-    const int32_t B = p->meta.block_size();
-    const bool grouped = shared && !p->shared.groups.empty();
-    p->plan = build_rows(p->rows, M, n, grouped, [&](int32_t r) {
-      const pkv::SeqMeta* q = p->meta.seq(seqs[r]);
-      RowIn in;
-      in.start = q->seq_len;
-      in.pt_off = static_cast<int32_t>(seqs[r] * p->stride);
-      const size_t pg = static_cast<size_t>(q->seq_len / B);
-      in.append_block = pg < q->pages.size() ? static_cast<int32_t>(q->pages[pg]) : -1;
-      if (shared) {
-        in.k_off = p->shared.k_off[r];
-        in.n_pre = p->shared.n_pre[r];
-      }
-      return in;
-    });
-    if (shared) append_shared(p->rows, p->shared, &p->plan);
-    // The patch kernel writes entries in parallel, so keep only the last
-    // write of each (sequence, page) entry (a fork's share followed by a
-    // copy-on-append replacement, for example).
-    p->patch_off = p->rows.size();
-    p->seen.clear();
-    for (auto it = pt.rbegin(); it != pt.rend(); ++it) {
-      if (!p->seen.insert(static_cast<int64_t>(it->seq) * p->stride + it->page).second)
-        continue;
-      p->rows.push_back(it->seq);
-      p->rows.push_back(it->page);
-      p->rows.push_back(it->block);
-    }
+    build_blob(p, seqs, M, n, shared_heads, p->rows, &p->plan, &p->patch_off);
     p->rows_key.clear();  // the blob below is new
   }
   const int32_t n_patch = static_cast<int32_t>((p->rows.size() - p->patch_off) / 3);
@@ -1028,6 +1041,61 @@ int32_t pkv_attn_with_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t 
     return rc;
   return pkv_attn_paged_decode(pool, seqs, M, layer, n_heads, n_kv_heads, head_dim, Q_dev,
                                scale, out_dev, ws_dev, ws_bytes, stream);
+}
+
+int32_t pkv_attn_paged_decode_noalloc(pkv_pool* pool, const int32_t* seqs, int32_t M,
+                                      int32_t layer, int32_t n_heads, int32_t n_kv_heads,
+                                      int32_t head_dim, const float* Q_dev, float scale,
+                                      float* out_dev, void* stream) {
+  // the checks of pkv_attn_paged_decode, in the same order (no workspace)
+  if (!pool) return PKV_ERR_BAD_ARG;
+  if (int32_t rc = attn_front_checks(M, 1, n_heads, n_kv_heads, head_dim)) return rc;
+  auto& m = pool->meta;
+  if (n_kv_heads != m.n_kv_heads() || head_dim != m.head_dim()) return PKV_ERR_BAD_DIM;
+  if (int32_t rc = m.check_batch(seqs, M)) return rc;
+  if (layer < 0 || layer >= m.n_layers()) return PKV_ERR_BAD_ARG;
+  if (!pool->storage) return PKV_ERR_BAD_ARG;
+  if (int32_t rc = m.check_rows(seqs, M, 1)) return rc;
+  if (int32_t rc = pool_rope_check(pool, seqs, M, 1)) return rc;
+  if (!Q_dev || !out_dev) return PKV_ERR_BAD_ARG;
+  // growing the page-table mirror would allocate
+  if (!pool->mirror || pkv::PoolMeta::mirror_stride(m.max_pages_seen()) > pool->stride)
+    return PKV_ERR_UNSUPPORTED;
+  RowPlan plan;
+  size_t patch_off = 0;
+  build_blob(pool, seqs, M, 1, 0, pool->na_rows, &plan, &patch_off);
+  const int32_t group = n_heads / n_kv_heads;
+  const size_t part = uses_splits(Kind::kDecode, head_dim, group, m.block_size(), 1)
+                          ? partial_bytes(plan, 1, n_heads, head_dim)
+                          : 0;
+  if (pool->na_rows.size() * sizeof(int32_t) > pkv::kNoAllocBlobBytes ||
+      part > pkv::kNoAllocPartBytes)
+    return PKV_ERR_CAPACITY;
+  void* base = nullptr;
+  if (pkv::noalloc_scratch(&base) != hipSuccess) return PKV_ERR_DEVICE;
+  const hipStream_t st = as_stream(stream);
+  if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
+  int32_t* blob = static_cast<int32_t*>(base);
+  float* ws = reinterpret_cast<float*>(static_cast<char*>(base) + pkv::kNoAllocBlobBytes);
+  if (pkv::launch_write_ints(blob, pool->na_rows.data(), pool->na_rows.size(), st) !=
+      hipSuccess)
+    return PKV_ERR_DEVICE;
+  const int32_t n_patch = static_cast<int32_t>((pool->na_rows.size() - patch_off) / 3);
+  if (n_patch > 0) {
+    if (pkv::launch_patch(pool->mirror, blob + patch_off, n_patch, pool->stride, st) !=
+        hipSuccess)
+      return PKV_ERR_DEVICE;
+    m.patches().clear();
+  }
+  pool->last_shared = false;
+  pool->shared_heads = 0;
+  pool->dev.no_new_events = true;
+  const int32_t rc = run_attention(pool->dev, make_paged_map(pool, layer), blob, plan, Q_dev,
+                                   out_dev, ws, n_heads, n_kv_heads, head_dim, 1, 1, scale,
+                                   M, m.block_size(), Kind::kDecode, rope_table(pool->rope),
+                                   st);
+  pool->dev.no_new_events = false;
+  return rc;
 }
 
 int32_t pkv_attn_paged_verify(pkv_pool* pool, const int32_t* seqs, int32_t M,

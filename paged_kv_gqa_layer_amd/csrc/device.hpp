@@ -210,4 +210,18 @@ hipError_t launch_prefill_mfma(const PagedMap& m, const AttnArgs& a,
 hipError_t launch_prefill_mfma(const ContigMap& m, const AttnArgs& a,
                                int32_t group, hipStream_t st);
 
+// Zero-allocation decode: a file-scope device array (one copy per GPU, held
+// until the process ends) with a row-blob region followed by a split-partial
+// region.
+constexpr size_t kNoAllocBlobBytes = size_t(1) << 20;
+constexpr size_t kNoAllocPartBytes = size_t(64) << 20;
+// Device address of the current GPU's scratch array (looked up once per
+// device, with that device current; later calls return the kept address).
+hipError_t noalloc_scratch(void** base);
+// Writes n ints from host memory to device memory dst by passing them as
+// kernel arguments (ceil(n / kIntChunk) launches, no staging buffer).
+constexpr int32_t kIntChunk = 896;
+hipError_t launch_write_ints(int32_t* dst, const int32_t* src, size_t n,
+                             hipStream_t st);
+
 }  // namespace pkv

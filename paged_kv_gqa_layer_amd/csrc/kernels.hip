@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "device.hpp"
 
@@ -1454,7 +1455,53 @@ hipError_t prefill_impl(const Map& m, const AttnArgs& a, int32_t group,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Zero-allocation decode support.  The scratch array is device memory the
+// library never allocates at run time: the code object carries it, and each
+// GPU gets its own copy when the library's kernels are loaded there.
+// ---------------------------------------------------------------------------
+struct IntChunk {
+  int32_t n;
+  int32_t v[kIntChunk];
+};
+
+__global__ __launch_bounds__(256) void write_ints_kernel(int32_t* dst, IntChunk c) {
+  const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < c.n) dst[i] = c.v[i];
+}
+
 }  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocBlobBytes + kNoAllocPartBytes];
+
+hipError_t noalloc_scratch(void** base) {
+  static std::mutex mu;
+  static void* addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *base = addr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_write_ints(int32_t* dst, const int32_t* src, size_t n, hipStream_t st) {
+  IntChunk c;
+  for (size_t off = 0; off < n; off += kIntChunk) {
+    c.n = static_cast<int32_t>(std::min<size_t>(kIntChunk, n - off));
+    std::copy(src + off, src + off + c.n, c.v);
+    write_ints_kernel<<<(c.n + 255) / 256, 256, 0, st>>>(dst + off, c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_patch(int32_t* mirror, const int32_t* patches, int32_t n,
                         int64_t stride, hipStream_t st) {
