@@ -254,7 +254,8 @@ def bench_decode(args, synth, pkv):
     # launch adds two event records to the stream, ~5-10 us per step).
     r = run(0, kernels=[pkv.K_DECODE])
     res = dict(r, wl=wl, pool=pool, seqs=seqs,
-               seq_tok_s=M * args.steps / r["elapsed"])
+               seq_tok_s=M * args.steps / r["elapsed"],
+               kernel_name=pool.kernel_name(pkv.K_DECODE))
     log("decode: %.3f ms/step, %.0f GB/s step, kernel %.1f us avg -> %.0f GB/s (%.1f%% of peak)"
         % (1e3 * r["elapsed"] / args.steps, r["gbs"], r["kern"]["decode"]["avg_us"],
            r["achieved"], 100 * r["achieved"] / HBM_PEAK_GBS))
@@ -397,81 +398,137 @@ def bench_verify(args, wl, pool, seqs, n_q, pkv, torch):
 def bench_forked(args, synth, pkv, shared):
     """The forked batch: one 2048-row prefix forked into 64 sequences (the
     parent then freed, so every prefix block has 64 references), each
-    decoding its own token stream, with pkv_attn_paged_decode or (shared)
-    pkv_attn_paged_decode_shared.  Times the decode steps after the first
-    `warmup`; reports logical KV bytes (every fork's visible keys) and unique
-    bytes (prefix once + each fork's own rows) per second."""
+    decoding its own token stream with pkv_attn_paged_decode or (shared)
+    pkv_attn_paged_decode_shared; then the rewind half: the even forks
+    truncate back to the fork point and replay their odd partner's stream,
+    every replayed output compared bit for bit with the partner's.
+
+    Both halves time their steps after `warmup` with HIP events on the
+    attention kernel only (as the decode headline); a second run of the
+    decode half with every launch timed gives the per-kernel breakdown.
+    Reports logical KV bytes (every sequence's visible keys) and unique
+    bytes (the prefix once + each sequence's own rows) per second."""
     import torch
     wl = synth.forked_2048x64()
     H, G, D, F = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.n_forks
-    pool = pkv.Pool(wl.n_blocks, wl.block_size, 1, G, D, max_seqs=F + 8)
-    pool.set_free_order(wl.free_order())
-    parent = pool.seq_new(wl.max_tokens)
-    pk, pv = wl.prefix_kv()
-    pool.ensure_append([parent], wl.prefix, check=True)
-    pool.append_layer([parent], wl.prefix, 0, torch.from_numpy(pk).cuda(),
-                      torch.from_numpy(pv).cuda(), check=True)
-    pool.advance([parent], wl.prefix, check=True)
-    forks = [pool.seq_fork(parent) for _ in range(F)]
-    pool.seq_free(parent, check=True)
-    seqs_np = np.asarray(forks, np.int32)
+    kv_row = 2 * wl.kv_dim * 4
 
     def step_inputs(t):
         xs = [wl.fork_step(f, t) for f in range(F)]
         return tuple(np.stack([x[i] for x in xs]) for i in range(3))
     inputs = [tuple(torch.from_numpy(a).cuda() for a in x)
               for x in synth.parallel_map(step_inputs, range(wl.steps))]
-    out = torch.empty((F, H * D), device="cuda")
-    # workspace: the library's own count for this batch, doubled for the
-    # rows the forks add over the steps (a few more 512-key splits at most)
-    ws_bytes = max(pool.decode_workspace_bytes(seqs_np, H),
-                   pool.decode_shared_workspace_bytes(seqs_np, H))
-    ws = torch.empty(2 * ws_bytes + 4, dtype=torch.uint8, device="cuda")
+    # the odd forks' inputs, replayed by the even forks in the rewind half
+    odd_inputs = [tuple(a[1::2].contiguous() for a in x) for x in inputs]
+    attn_id = pkv.K_PREFIX if shared else pkv.K_DECODE
 
-    attn = pool.attn_paged_decode_shared if shared else pool.attn_paged_decode
+    def run(kernels):
+        pool = pkv.Pool(wl.n_blocks, wl.block_size, 1, G, D, max_seqs=F + 8)
+        pool.set_free_order(wl.free_order())
+        parent = pool.seq_new(wl.max_tokens)
+        pk, pv = wl.prefix_kv()
+        pool.ensure_append([parent], wl.prefix, check=True)
+        pool.append_layer([parent], wl.prefix, 0, torch.from_numpy(pk).cuda(),
+                          torch.from_numpy(pv).cuda(), check=True)
+        pool.advance([parent], wl.prefix, check=True)
+        forks = [pool.seq_fork(parent) for _ in range(F)]
+        pool.seq_free(parent, check=True)
+        seqs_np = np.asarray(forks, np.int32)
+        evens_np = seqs_np[0::2].copy()
+        outs = torch.empty((wl.steps, F, H * D), device="cuda")
+        # workspace: the library's own count for this batch, doubled for the
+        # rows the forks add over the steps (a few more splits at most)
+        ws_bytes = max(pool.decode_workspace_bytes(seqs_np, H),
+                       pool.decode_shared_workspace_bytes(seqs_np, H))
+        ws = torch.empty(2 * ws_bytes + 4, dtype=torch.uint8, device="cuda")
+        attn = pool.attn_paged_decode_shared if shared else pool.attn_paged_decode
 
-    def step(t):
-        q, k, v = inputs[t]
-        pool.ensure_append(seqs_np, 1, check=True)
-        pool.append_layer(seqs_np, 1, 0, k, v, check=True)
-        attn(seqs_np, 0, H, G, D, q, wl.scale, out, ws=ws, check=True)
-        pool.advance(seqs_np, 1, check=True)
+        def step(batch, inp, out):
+            q, k, v = inp
+            pool.ensure_append(batch, 1, check=True)
+            pool.append_layer(batch, 1, 0, k, v, check=True)
+            attn(batch, 0, H, G, D, q, wl.scale, out, ws=ws, check=True)
+            pool.advance(batch, 1, check=True)
 
-    w = min(args.warmup, wl.steps - 1)
-    pool.profile_enable(True)  # warm-up with the timing events on (see run())
-    for t in range(w):
-        step(t)
-    torch.cuda.synchronize()
-    pool.profile_enable(True)
-    t0 = time.perf_counter()
-    for t in range(w, wl.steps):
-        step(t)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    kern = {}
-    for name, kid in (("append", pkv.K_APPEND), ("shared_decode", pkv.K_PREFIX),
-                      ("decode", pkv.K_DECODE), ("merge", pkv.K_MERGE),
-                      ("cow", pkv.K_COW)):
-        ms, n = pool.profile_read(kid)
-        kern[name] = (1e3 * ms / n) if n else 0.0
-    pool.profile_enable(False)
-    n = wl.steps - w
-    logical = sum(F * (wl.prefix + t + 1) for t in range(w, wl.steps)) * 2 * wl.kv_dim * 4
-    unique = sum(wl.prefix + F * (t + 1) for t in range(w, wl.steps)) * 2 * wl.kv_dim * 4
-    pool.close()
-    res = {
-        "workload": wl.name, "forks": F, "prefix": wl.prefix, "steps": n,
-        "ms_per_step": 1e3 * elapsed / n,
-        "logical_gbs": logical / elapsed / 1e9, "unique_gbs": unique / elapsed / 1e9,
-        "seq_tokens_per_s": F * n / elapsed, "kernels_us": kern,
-        "step": "ensure_append + append_layer + %s + advance"
-                % ("attn_paged_decode_shared" if shared else "attn_paged_decode"),
-    }
-    log("forked%s: %.3f ms/step, logical %.0f GB/s, unique %.0f GB/s, %s %.1f us, "
-        "merge %.1f us"
+        def timed(batch, inps, outs_):
+            w = min(args.warmup, wl.steps - 1)
+            pool.profile_kernels(kernels)
+            pool.profile_enable(True)  # warm-up with the timing events on
+            for t in range(w):
+                step(batch, inps[t], outs_[t])
+            torch.cuda.synchronize()
+            pool.profile_enable(True)
+            t0 = time.perf_counter()
+            for t in range(w, wl.steps):
+                step(batch, inps[t], outs_[t])
+            torch.cuda.synchronize()
+            elapsed = time.perf_counter() - t0
+            kern = {}
+            for name, kid in (("append", pkv.K_APPEND), ("shared_decode", pkv.K_PREFIX),
+                              ("decode", pkv.K_DECODE), ("merge", pkv.K_MERGE),
+                              ("cow", pkv.K_COW)):
+                ms, n = pool.profile_read(kid)
+                if n:
+                    kern[name] = 1e3 * ms / n
+            att_us = 1e3 * pool.profile_samples(attn_id)
+            pool.profile_enable(False)
+            pool.profile_kernels(None)
+            return w, elapsed, kern, att_us
+
+        w, el, kern, att_us = timed(seqs_np, inputs, outs)
+        n = wl.steps - w
+        logical = sum(F * (wl.prefix + t + 1) for t in range(w, wl.steps)) * kv_row
+        unique = sum(wl.prefix + F * (t + 1) for t in range(w, wl.steps)) * kv_row
+        res = {
+            "ms_per_step": 1e3 * el / n, "steps": n,
+            "logical_gbs": logical / el / 1e9, "unique_gbs": unique / el / 1e9,
+            "seq_tokens_per_s": F * n / el, "kernels_us": kern,
+            "attention_kernel": pool.kernel_name(attn_id),
+            "attention_kernel_us_percentiles": pct(att_us),
+        }
+        if kernels is None:
+            pool.close()
+            return res
+        # rewind half: even forks go back to the fork point and replay the
+        # odd forks' streams
+        for s in evens_np:
+            pool.seq_truncate(int(s), wl.prefix, check=True)
+        routs = torch.empty((wl.steps, F // 2, H * D), device="cuda")
+        w, el, kern, att_us = timed(evens_np, odd_inputs, routs)
+        torch.cuda.synchronize()
+        same = [bool(torch.equal(routs[t].view(torch.int32),
+                                 outs[t, 1::2].contiguous().view(torch.int32)))
+                for t in range(wl.steps)]
+        n = wl.steps - w
+        R = F // 2
+        res["rewind"] = {
+            "ms_per_step": 1e3 * el / n, "steps": n, "sequences": R,
+            "logical_gbs": sum(R * (wl.prefix + t + 1) for t in range(w, wl.steps))
+            * kv_row / el / 1e9,
+            "unique_gbs": sum(wl.prefix + R * (t + 1) for t in range(w, wl.steps))
+            * kv_row / el / 1e9,
+            "kernels_us": kern, "attention_kernel_us_percentiles": pct(att_us),
+            "bitwise_equal_steps": int(sum(same)), "checked_steps": wl.steps,
+            "step": "even forks truncated to the fork point, then ensure_append + "
+                    "append_layer + attention + advance on the odd partner's inputs",
+        }
+        pool.close()
+        return res
+
+    res = run([attn_id])
+    res.update({"workload": wl.name, "forks": F, "prefix": wl.prefix,
+                "step": "ensure_append + append_layer + %s + advance"
+                        % ("attn_paged_decode_shared" if shared else "attn_paged_decode")})
+    bd = run(None)
+    res["breakdown"] = {"ms_per_step": bd["ms_per_step"], "kernels_us": bd["kernels_us"],
+                        "step": "as the decode half, every kernel launch timed"}
+    log("forked%s: %.4f ms/step, logical %.0f GB/s, unique %.0f GB/s, %s p50 %.1f us; "
+        "rewind %.4f ms/step, bitwise %d/%d; all timed %.4f ms/step %s"
         % (" shared" if shared else "", res["ms_per_step"], res["logical_gbs"],
-           res["unique_gbs"], "shared_decode" if shared else "decode",
-           kern["shared_decode" if shared else "decode"], kern["merge"]))
+           res["unique_gbs"], res["attention_kernel"],
+           res["attention_kernel_us_percentiles"]["p50"], res["rewind"]["ms_per_step"],
+           res["rewind"]["bitwise_equal_steps"], res["rewind"]["checked_steps"],
+           bd["ms_per_step"], json.dumps(bd["kernels_us"])))
     return res
 
 
@@ -532,44 +589,52 @@ def cpu_baseline(args, wl, oracle):
     }
 
 
-def cpu_baseline_prefill(synth, oracle, n_last=16):
+def cpu_baseline_prefill(synth, oracle, n_last=64):
     """The oracle on a sample of the prefill workload: the last n_last chunk
-    queries of every sequence (each sees ~4K keys), one oracle call per
-    sequence; once on one thread, then over the host cores.  Reported in
-    TFLOP/s of the same algorithmic flops as the kernel (4 * D * H per
-    visible key)."""
+    queries of every sequence (each sees ~4K keys), cut into (sequence,
+    query head) units -- one oracle call per unit over that head's queries
+    and its kv head's K/V columns -- run once on one thread, then over every
+    host core available to this process.  Reported in TFLOP/s of the same
+    algorithmic flops as the kernel (4 * D per visible key and head)."""
     from concurrent.futures import ThreadPoolExecutor
     wl = synth.prefill_8x3584p512()
     H, G, D = wl.n_heads, wl.n_kv_heads, wl.head_dim
-    sample = []
+    group = H // G
+    units = []
     for r in range(wl.M):
         kh, vh = wl.history(r)
         q, k, v = wl.chunk_inputs(r)
-        sample.append((q[-n_last:], np.concatenate([kh, k]), np.concatenate([vh, v])))
+        K = np.concatenate([kh, k])
+        V = np.concatenate([vh, v])
+        for h in range(H):
+            c = h // group
+            units.append((np.ascontiguousarray(q[-n_last:, h * D:(h + 1) * D]),
+                          np.ascontiguousarray(K[:, c * D:(c + 1) * D]),
+                          np.ascontiguousarray(V[:, c * D:(c + 1) * D])))
     total_k = wl.cached + wl.chunk
     flops = wl.M * sum(4 * D * H * (total_k - n_last + i + 1) for i in range(n_last))
 
     def one(item):
         q, K, V = item
-        rc, _ = oracle.attn_contig(q, K, V, H, G, D, True, wl.scale)
+        rc, _ = oracle.attn_contig(q, K, V, 1, 1, D, True, wl.scale)
         assert rc == 0
 
     t0 = time.perf_counter()
-    for item in sample:
+    for item in units:
         one(item)
     t1 = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=cores) as ex:
-        list(ex.map(one, sample))
+        list(ex.map(one, units))
     tn = time.perf_counter() - t0
-    log("cpu oracle, prefill: %d queries: %.2fs on one thread, %.2fs on %d threads"
-        % (wl.M * n_last, t1, tn, min(cores, wl.M)))
+    log("cpu oracle, prefill: %d (sequence, head) units: %.2fs on one thread, %.2fs on %d threads"
+        % (len(units), t1, tn, cores))
     return {
-        "value": flops / tn / 1e12, "unit": "TFLOP/s", "cores": min(cores, wl.M),
-        "kind": "oracle",
-        "sample": "last %d chunk queries of each of the %d sequences (%.2e flop), one "
-                  "oracle call per sequence per thread" % (n_last, wl.M, flops),
+        "value": flops / tn / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": "last %d chunk queries of each of the %d sequences (%.2e flop), as %d "
+                  "(sequence, query head) oracle calls over the host cores"
+                  % (n_last, wl.M, flops, len(units)),
         "one_thread": {"value": flops / t1 / 1e12, "unit": "TFLOP/s", "cores": 1},
     }
 
@@ -612,14 +677,18 @@ def bench_decode_small(args, synth, pkv):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms, n = pool.profile_read(pkv.K_DECODE)
+    dec_us = 1e3 * pool.profile_samples(pkv.K_DECODE)
+    kname = pool.kernel_name(pkv.K_DECODE)
     pool.profile_enable(False)
     pool.close()
     kv_bytes = sum(int((wl.ctx.astype(np.int64) + t + 1).sum()) * 2 * wl.kv_dim * 4
                    for t in range(args.warmup, n_steps))
     res = {
         "workload": wl.name, "M": M, "ms_per_step": 1e3 * elapsed / args.steps,
-        "gbs": kv_bytes / elapsed / 1e9, "kernel_us": 1e3 * ms / n,
+        "gbs": kv_bytes / elapsed / 1e9, "pct_hbm_peak": 100 * kv_bytes / elapsed / 1e9
+        / HBM_PEAK_GBS, "kernel_us": 1e3 * ms / n,
         "kernel_gbs": kv_bytes / (ms * 1e-3) / 1e9, "seq_tokens_per_s": M * args.steps / elapsed,
+        "kernel": kname, "decode_kernel_us_percentiles": pct(dec_us),
         "step": "ensure_append + append_layer + attn_paged_decode + advance",
     }
     log("decode M=32: %.3f ms/step, %.0f GB/s step, kernel %.1f us -> %.0f GB/s"
@@ -668,6 +737,8 @@ def bench_prefill(args, synth, pkv):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms, n = pool.profile_read(pkv.K_PREFILL)
+    kern_ms = pool.profile_samples(pkv.K_PREFILL)
+    kname = pool.kernel_name(pkv.K_PREFILL)
     pool.profile_enable(False)
     visible = M * sum(wl.cached + i + 1 for i in range(wl.chunk))
     flops = 4 * D * H * visible
@@ -684,10 +755,11 @@ def bench_prefill(args, synth, pkv):
         "steps": args.prefill_steps,
         "step": "ensure_append(512) + append_layer + attn_paged_prefill + truncate",
         "kernel_ms": 1e3 * kern_s, "flops_per_step": flops,
+        "kernel_ms_percentiles": pct(kern_ms),
         "roofline": {"bound": "mfma", "achieved": tf, "peak": FP32_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": tf / FP32_MFMA_PEAK_TFLOPS,
                      "traffic": traffic_for("prefill_mfma_kernel", unique_bytes),
-                     "unique_bytes_per_launch": unique_bytes},
+                     "kernel": kname, "unique_bytes_per_launch": unique_bytes},
     }
 
 
@@ -751,7 +823,7 @@ def main():
             "bound": "hbm", "achieved": d["achieved"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": d["achieved"] / HBM_PEAK_GBS,
             "traffic": (traffic if traffic is not None else None),
-            "kernel": "decode_fast_kernel<4, PagedMap, true>",
+            "kernel": d["kernel_name"],
             "bytes_per_launch": d["kv_bytes"] / args.steps,
         },
     }

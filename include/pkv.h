@@ -510,6 +510,14 @@ int32_t pkv_profile_kernels(pkv_pool *pool, uint32_t mask);
 int32_t pkv_profile_read(pkv_pool *pool, int32_t kernel, double *total_ms,
                          int64_t *launches);
 
+/* The kernel form last launched under kernel id `kernel` -- the template
+ * instance, e.g. "decode_fast_kernel<4, PagedMap, true>" (GQA group, address
+ * map, deep form) -- written NUL-terminated into out[0..cap) (truncated to
+ * fit).  Returns the name's full length (0 before any launch) or a negated
+ * code.  Recorded whether or not profiling is on. */
+int32_t pkv_profile_kernel_name(pkv_pool *pool, int32_t kernel, char *out,
+                                int32_t cap);
+
 /* Wait for the recorded events and copy the duration (ms) of each of the
  * first cap launches of one kernel id, in launch order; returns the number
  * of launches recorded (which may exceed cap) or a negated code. */

@@ -344,6 +344,15 @@ class Pool:
             raise PKVError(-n, "profile_samples")
         return out[:n].astype(np.float64)
 
+    def kernel_name(self, kernel):
+        """The kernel form last launched under a kernel id ('' if none)."""
+        n = lib().pkv_profile_kernel_name(self._h, kernel, None, 0)
+        if n < 0:
+            raise PKVError(-n, "profile_kernel_name")
+        buf = C.create_string_buffer(n + 1)
+        lib().pkv_profile_kernel_name(self._h, kernel, buf, n + 1)
+        return buf.value.decode()
+
     def profile_read(self, kernel):
         ms = C.c_double(0.0)
         n = C.c_int64(0)

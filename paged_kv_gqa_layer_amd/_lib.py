@@ -89,6 +89,7 @@ SIGNATURES = {
     "pkv_profile_read": (_I32, [_P, _I32, C.POINTER(C.c_double),
                                 C.POINTER(C.c_int64)]),
     "pkv_profile_samples": (_I32, [_P, _I32, _P, _I32]),
+    "pkv_profile_kernel_name": (_I32, [_P, _I32, C.c_char_p, _I32]),
 }
 
 _lib = None

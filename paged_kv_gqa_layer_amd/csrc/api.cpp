@@ -19,6 +19,7 @@
 #include <cstring>
 #include <functional>
 #include <mutex>
+#include <string>
 #include <type_traits>
 #include <unordered_map>
 #include <unordered_set>
@@ -54,6 +55,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 struct DeviceCtx {
   struct Slot {
     void* host = nullptr;
+    const void* dev = nullptr;  // the same memory as kernels address it
     size_t cap = 0;
     hipEvent_t ev = nullptr;
     bool pending = false;
@@ -66,6 +68,7 @@ struct DeviceCtx {
   };
   Slot slot[kStageSlots];
   int next = 0;
+  int last_slot = 0;  // the slot take_slot returned last
   DevBuf buf[kNumBufs];
   hipStream_t last_stream = nullptr;
   bool used = false;
@@ -74,6 +77,8 @@ struct DeviceCtx {
   uint32_t prof_mask = ~0u;  // kernel ids timed while prof_on
   // while set, timing uses only events made earlier (none are created)
   bool no_new_events = false;
+  // the kernel form (template instance) last launched under each kernel id
+  std::string form[PKV_K_COUNT];
   std::vector<std::pair<hipEvent_t, hipEvent_t>> prof_ev[PKV_K_COUNT];
   // Timing events of earlier profiling runs, reused (creating timing events
   // can cost the host more than a short step).
@@ -159,6 +164,38 @@ struct DeviceCtx {
     return hipSuccess;
   }
 
+  // The next staging slot, free for rewriting (its previous reader done),
+  // with room for `bytes`.
+  hipError_t take_slot(size_t bytes, Slot** out) {
+    Slot& s = slot[next];
+    last_slot = next;
+    next = (next + 1) % kStageSlots;
+    hipError_t e;
+    if (s.pending) {
+      if ((e = hipEventSynchronize(s.ev)) != hipSuccess) return e;
+      s.pending = false;
+    }
+    if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess)
+      return e;
+    if (bytes > s.cap) {
+      if (s.host) (void)hipHostFree(s.host);
+      s.host = nullptr;
+      s.dev = nullptr;
+      s.cap = 0;
+      const size_t cap = bytes < 65536 ? 65536 : bytes + bytes / 2;
+      // coherent: kernels read the slot directly and must see every rewrite
+      if ((e = hipHostMalloc(&s.host, cap, hipHostMallocMapped | hipHostMallocCoherent)) !=
+          hipSuccess)
+        return e;
+      void* dp = nullptr;
+      if ((e = hipHostGetDevicePointer(&dp, s.host, 0)) != hipSuccess) return e;
+      s.dev = dp;
+      s.cap = cap;
+    }
+    *out = &s;
+    return hipSuccess;
+  }
+
   // Copy `blob` into device buffer `b` (skipped if it already holds `key`;
   // an empty key never matches).
   hipError_t upload(int b, const std::vector<int32_t>& blob,
@@ -173,34 +210,54 @@ struct DeviceCtx {
     const size_t bytes = std::max<size_t>(blob.size(), 1) * sizeof(int32_t);
     hipError_t e = reserve(b, bytes, st);
     if (e != hipSuccess) return e;
-    Slot& s = slot[next];
-    next = (next + 1) % kStageSlots;
-    if (s.pending) {
-      if ((e = hipEventSynchronize(s.ev)) != hipSuccess) return e;
-      s.pending = false;
-    }
-    if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess)
-      return e;
-    if (bytes > s.cap) {
-      if (s.host) (void)hipHostFree(s.host);
-      s.host = nullptr;
-      s.cap = 0;
-      const size_t cap = bytes < 65536 ? 65536 : bytes + bytes / 2;
-      if ((e = hipHostMalloc(&s.host, cap, hipHostMallocDefault)) != hipSuccess) return e;
-      s.cap = cap;
-    }
+    Slot* s = nullptr;
+    if ((e = take_slot(bytes, &s)) != hipSuccess) return e;
     if (!blob.empty()) {
-      std::memcpy(s.host, blob.data(), blob.size() * sizeof(int32_t));
-      if ((e = hipMemcpyAsync(d.ptr, s.host, blob.size() * sizeof(int32_t),
+      std::memcpy(s->host, blob.data(), blob.size() * sizeof(int32_t));
+      if ((e = hipMemcpyAsync(d.ptr, s->host, blob.size() * sizeof(int32_t),
                               hipMemcpyHostToDevice, st)) != hipSuccess)
         return e;
-      if ((e = hipEventRecord(s.ev, st)) != hipSuccess) return e;
-      s.pending = true;
+      if ((e = hipEventRecord(s->ev, st)) != hipSuccess) return e;
+      s->pending = true;
     }
     d.key = key;
     d.valid = !key.empty();
     *dev = static_cast<int32_t*>(d.ptr);
     return hipSuccess;
+  }
+
+  // As upload, but the copy into device buffer `b` is left to the caller's
+  // next kernel: the blob goes to a pinned staging slot which that kernel
+  // reads (*src, a device-readable address) and copies to *dev.  *src is
+  // null when buffer b already holds `key` (nothing to copy).  After the
+  // kernel is enqueued, staged(st) marks the slot busy until it has run.
+  hipError_t stage(int b, const std::vector<int32_t>& blob,
+                   const std::vector<int64_t>& key, hipStream_t st,
+                   const int32_t** src, int32_t** dev) {
+    DevBuf& d = buf[b];
+    *src = nullptr;
+    if (!key.empty() && d.valid && d.key == key) {
+      *dev = static_cast<int32_t*>(d.ptr);
+      return hipSuccess;
+    }
+    d.valid = false;
+    const size_t bytes = std::max<size_t>(blob.size(), 1) * sizeof(int32_t);
+    hipError_t e = reserve(b, bytes, st);
+    if (e != hipSuccess) return e;
+    Slot* s = nullptr;
+    if ((e = take_slot(bytes, &s)) != hipSuccess) return e;
+    if (!blob.empty()) std::memcpy(s->host, blob.data(), blob.size() * sizeof(int32_t));
+    d.key = key;
+    d.valid = !key.empty();
+    *src = static_cast<const int32_t*>(s->dev);
+    *dev = static_cast<int32_t*>(d.ptr);
+    return hipSuccess;
+  }
+  hipError_t staged(hipStream_t st) {
+    Slot& s = slot[last_slot];
+    const hipError_t e = hipEventRecord(s.ev, st);
+    if (e == hipSuccess) s.pending = true;
+    return e;
   }
 
   // Timing brackets around one launch.
@@ -521,9 +578,14 @@ void build_blob(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
 // travel in one upload, which is skipped when the device copy already
 // describes this batch at this pool version (no patches can be pending then:
 // every page-table change bumps the version).
+// With `fused` (the one-row append), both the upload and the patches are
+// left to the caller's kernel: *rows_dev is then the copy that kernel reads
+// (the pinned staging copy when an upload is due), *fused says what it must
+// copy and patch, and the caller calls p->dev.staged(st) after the launch
+// when fused->n_copy > 0.
 hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
                      int32_t shared_heads, hipStream_t st, const int32_t** rows_dev,
-                     pkv::PatchArgs* deferred = nullptr) {
+                     pkv::PatchArgs* fused = nullptr) {
   hipError_t e = size_mirror(p, st);
   if (e != hipSuccess) return e;
   std::vector<int64_t> key;
@@ -540,16 +602,26 @@ hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
   }
   const int32_t n_patch = static_cast<int32_t>((p->rows.size() - p->patch_off) / 3);
   int32_t* d = nullptr;
+  if (fused) {
+    const int32_t* src = nullptr;
+    if ((e = p->dev.stage(kRows, p->rows, key, st, &src, &d)) != hipSuccess) return e;
+    const int32_t* from = src ? src : d;
+    *fused = pkv::PatchArgs{p->mirror, from + p->patch_off, 0, p->stride, src, d,
+                            src ? static_cast<int32_t>(p->rows.size()) : 0};
+    if (!pt.empty()) {
+      pt.clear();
+      fused->n = n_patch;  // the caller's launch applies them
+    }
+    p->rows_key = key;
+    *rows_dev = from;
+    return hipSuccess;
+  }
   if ((e = p->dev.upload(kRows, p->rows, key, st, &d)) != hipSuccess) return e;
-  if (deferred) *deferred = pkv::PatchArgs{p->mirror, d + p->patch_off, 0, p->stride};
   if (!pt.empty()) {
     pt.clear();
-    if (deferred) {
-      deferred->n = n_patch;  // the caller's launch applies them
-    } else if ((e = pkv::launch_patch(p->mirror, d + p->patch_off, n_patch, p->stride,
-                                      st)) != hipSuccess) {
+    if ((e = pkv::launch_patch(p->mirror, d + p->patch_off, n_patch, p->stride, st)) !=
+        hipSuccess)
       return e;
-    }
   }
   p->rows_key = key;
   *rows_dev = d;
@@ -643,39 +715,55 @@ int32_t run_attention(DeviceCtx& dev, const Map& map, const int32_t* rows_dev,
   a.members = rows_dev + pl.member_off;
   a.n_pre_items = pl.n_pre_items;
   hipError_t e;
+  const char* mname = std::is_same<Map, PagedMap>::value ? "PagedMap" : "ContigMap";
+  auto name = [](const char* kernel, std::initializer_list<std::string> args) {
+    std::string n = std::string(kernel) + "<";
+    for (const auto& x : args) n += (n.back() == '<' ? "" : ", ") + x;
+    return n + ">";
+  };
   if (uses_splits(kind, head_dim, group, block_size, n_q)) {
     if (pl.n_pre_items > 0) {
       // shared prefixes: the prefix work and the own-key splits in one launch
       if constexpr (std::is_same<Map, PagedMap>::value) {
+        dev.form[PKV_K_PREFIX] = name("shared_decode_kernel", {std::to_string(group)});
         {
           DeviceCtx::ProfScope ps(&dev, PKV_K_PREFIX, st);
           if (pkv::launch_shared_decode(map, a, group, st) != hipSuccess)
             return PKV_ERR_DEVICE;
         }
+        dev.form[PKV_K_MERGE] = "merge_kernel";
         DeviceCtx::ProfScope ps(&dev, PKV_K_MERGE, st);
         return dev_status(pkv::launch_merge(a, st));
       }
     }
     {
       const bool one = n_q == 1 && pkv::fast_decode_ok(head_dim, group, block_size);
-      DeviceCtx::ProfScope ps(&dev, one ? PKV_K_DECODE : PKV_K_VERIFY, st);
-      e = one ? pkv::launch_decode_fast(map, a, group,
-                                        pl.max_split >= 4 * pkv::kDecodeSplit, st)
+      const bool deep = pl.max_split >= 4 * pkv::kDecodeSplit;
+      const int kid = one ? PKV_K_DECODE : PKV_K_VERIFY;
+      dev.form[kid] = one ? name("decode_fast_kernel", {std::to_string(group), mname,
+                                                        deep ? "true" : "false"})
+                          : name("verify_mfma_kernel",
+                                 {n_q * group <= 16 ? "1" : "2", mname});
+      DeviceCtx::ProfScope ps(&dev, kid, st);
+      e = one ? pkv::launch_decode_fast(map, a, group, deep, st)
               : pkv::launch_verify_mfma(map, a, group, st);
       if (e != hipSuccess) return PKV_ERR_DEVICE;
     }
     if (pl.max_parts <= 1) return PKV_OK;
+    dev.form[PKV_K_MERGE] = "merge_kernel";
     DeviceCtx::ProfScope ps(&dev, PKV_K_MERGE, st);
     return dev_status(pkv::launch_merge(a, st));
   }
   const bool decode = kind == Kind::kDecode || kind == Kind::kDecodeShared;
   if (!decode && pkv::fast_prefill_ok(head_dim, group, block_size)) {
+    dev.form[PKV_K_PREFILL] = name("prefill_mfma_kernel", {std::to_string(group), mname});
     DeviceCtx::ProfScope ps(&dev, PKV_K_PREFILL, st);
     return dev_status(pkv::launch_prefill_mfma(map, a, group, st));
   }
   if (group > 16) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(group) * head_dim * 2 + group * 64 > 16384)
     return PKV_ERR_UNSUPPORTED;  // generic kernel keeps q and o in LDS
+  dev.form[decode ? PKV_K_DECODE : PKV_K_PREFILL] = name("generic_kernel", {mname});
   DeviceCtx::ProfScope ps(&dev, decode ? PKV_K_DECODE : PKV_K_PREFILL, st);
   return dev_status(pkv::launch_generic(map, a, group, st));
 }
@@ -860,6 +948,7 @@ int32_t pkv_ensure_append(pkv_pool* pool, const int32_t* seqs, int32_t M,
   }
   int32_t* dev = nullptr;
   if (pool->dev.upload(kCow, pairs, {}, st, &dev) != hipSuccess) return PKV_ERR_DEVICE;
+  pool->dev.form[PKV_K_COW] = pool->block_floats % 4 == 0 ? "cow_kernel<4>" : "cow_kernel<1>";
   DeviceCtx::ProfScope ps(&pool->dev, PKV_K_COW, st);
   return dev_status(pkv::launch_cow(pool->storage, dev,
                                     static_cast<int32_t>(cows.size()),
@@ -885,19 +974,35 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   const int32_t shared_heads =
       pool->last_shared && n_new == 1 ? pool->shared_heads : 0;
   // one row per sequence: the rows name the blocks they land in, so the
-  // append kernel also applies the pending page-table patches
+  // append kernel also applies the pending page-table patches and brings
+  // the step's row blob to the device
   pkv::PatchArgs pa{};
   if (pool_rows(pool, seqs, M, n_new, shared_heads, st, &rows,
                 n_new == 1 ? &pa : nullptr) != hipSuccess)
     return PKV_ERR_DEVICE;
   const PagedMap pm = make_paged_map(pool, layer);
   const int32_t kv_dim = pool->meta.n_kv_heads() * pool->meta.head_dim();
+  const int32_t span = pool->rope ? pool->meta.head_dim() / 2 : pool->meta.head_dim();
+  pool->dev.form[PKV_K_APPEND] = std::string("append_kernel<") +
+                                 (span % 4 == 0 ? "4" : "1") + ", PagedMap, " +
+                                 (pool->rope ? "true" : "false") + ", " +
+                                 (n_new == 1 ? "true" : "false") + ">";
+  if (n_new == 1) {
+    hipError_t e;
+    {
+      DeviceCtx::ProfScope ps(&pool->dev, PKV_K_APPEND, st);
+      e = pkv::launch_append_one(pm, reinterpret_cast<const RowDesc*>(rows), K_new_dev,
+                                 V_new_dev, M, kv_dim, pool->meta.head_dim(),
+                                 rope_table(pool->rope), pa, st);
+    }
+    if (e == hipSuccess && pa.n_copy > 0) e = pool->dev.staged(st);
+    if (e != hipSuccess) {  // the device blob was never written
+      pool->dev.buf[kRows].valid = false;
+      pool->rows_key.clear();
+    }
+    return dev_status(e);
+  }
   DeviceCtx::ProfScope ps(&pool->dev, PKV_K_APPEND, st);
-  if (n_new == 1)
-    return dev_status(pkv::launch_append_one(pm, reinterpret_cast<const RowDesc*>(rows),
-                                             K_new_dev, V_new_dev, M, kv_dim,
-                                             pool->meta.head_dim(), rope_table(pool->rope),
-                                             pa, st));
   return dev_status(pkv::launch_append(
       pm, reinterpret_cast<const RowDesc*>(rows), K_new_dev, V_new_dev, M, n_new,
       kv_dim, pool->meta.head_dim(), rope_table(pool->rope), st));
@@ -1347,6 +1452,18 @@ int32_t pkv_profile_read(pkv_pool* pool, int32_t kernel, double* total_ms,
   *total_ms = sum;
   *launches = static_cast<int64_t>(pool->dev.prof_ev[kernel].size());
   return PKV_OK;
+}
+
+int32_t pkv_profile_kernel_name(pkv_pool* pool, int32_t kernel, char* out, int32_t cap) {
+  if (!pool || kernel < 0 || kernel >= PKV_K_COUNT || (cap > 0 && !out))
+    return -PKV_ERR_BAD_ARG;
+  const std::string& f = pool->dev.form[kernel];
+  if (cap > 0) {
+    const size_t n = std::min<size_t>(f.size(), static_cast<size_t>(cap) - 1);
+    std::memcpy(out, f.data(), n);
+    out[n] = '\0';
+  }
+  return static_cast<int32_t>(f.size());
 }
 
 int32_t pkv_profile_samples(pkv_pool* pool, int32_t kernel, float* out_ms,

@@ -160,16 +160,23 @@ hipError_t launch_append(const ContigMap& m, const RowDesc* rows,
                          const float* K, const float* V, int32_t M, int32_t n,
                          int32_t kv_dim, int32_t head_dim, const double2* rope,
                          hipStream_t st);
-// Page-table mirror patches (seq, page, block triples) applied by a launch.
+// Page-table mirror patches (seq, page, block triples) applied by a launch,
+// and the row blob it copies to the device on the way (n_copy ints from
+// copy_src, device-readable pinned host memory, to copy_dst; n_copy = 0: no
+// copy).
 struct PatchArgs {
   int32_t* mirror;
   const int32_t* patches;
   int32_t n;
   int64_t stride;
+  const int32_t* copy_src;
+  int32_t* copy_dst;
+  int32_t n_copy;
 };
 // One new row per sequence, written to each RowDesc's append_block, with the
-// pending mirror patches applied by the same launch (the append does not
-// read the mirror).
+// pending mirror patches applied and the row blob copied by the same launch
+// (the append does not read the mirror; rows and patches may sit in the
+// pinned host copy of the blob).
 hipError_t launch_append_one(const PagedMap& m, const RowDesc* rows,
                              const float* K, const float* V, int32_t M,
                              int32_t kv_dim, int32_t head_dim,

@@ -129,6 +129,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (i < pa.n)
       pa.mirror[pa.patches[3 * i] * pa.stride + pa.patches[3 * i + 1]] = pa.patches[3 * i + 2];
+    if (i < pa.n_copy) pa.copy_dst[i] = pa.copy_src[i];
   }
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
@@ -1351,9 +1352,10 @@ hipError_t append_impl(const Map& m, const RowDesc* rows, const float* K,
   const int32_t span = rope ? head_dim / 2 : head_dim;
   const bool vec = (span % 4 == 0);
   const int64_t total = (int64_t)M * n * (rope ? kv_dim / 2 : kv_dim) / (vec ? 4 : 1);
-  const int64_t want = (std::max<int64_t>(total, pa.n) + 255) / 256;
+  const int64_t want = (std::max<int64_t>({total, pa.n, pa.n_copy}) + 255) / 256;
   const int grid = static_cast<int>(want < 65536 ? (want > 0 ? want : 1) : 65536);
-  if (ONE && (int64_t)grid * 256 < pa.n) return hipErrorInvalidValue;
+  if (ONE && ((int64_t)grid * 256 < pa.n || (int64_t)grid * 256 < pa.n_copy))
+    return hipErrorInvalidValue;
   if (rope && vec)
     append_kernel<4, Map, true, ONE><<<grid, 256, 0, st>>>(m, rows, K, V, n, kv_dim,
                                                            head_dim, total, cs, pa);

@@ -531,3 +531,17 @@ def test_prefill_mfma_other_groups_vs_oracle_and_contiguous(H, cached, n_q, caus
     cc.attn_prefill([0, 1], lens, n_q, 0, H, dev(Q), causal, scale, cout)
     torch.cuda.synchronize()
     assert bits_equal(out, cout)
+
+
+def test_kernel_forms_recorded():
+    """pkv_profile_kernel_name names the template instance each kernel id
+    launched last (the bench's roofline entry reads it)."""
+    wl = synth.decode_m32(max_steps=2)
+    pool, seqs = decode_pool(wl)
+    assert pool.kernel_name(pkv.K_DECODE) == ""
+    q, k, v = wl.step(0)
+    decode_step(pool, seqs, q, k, v, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.scale)
+    assert pool.kernel_name(pkv.K_DECODE) == "decode_fast_kernel<4, PagedMap, false>"
+    assert pool.kernel_name(pkv.K_MERGE) == "merge_kernel"
+    assert pool.kernel_name(pkv.K_APPEND) == "append_kernel<4, PagedMap, false, true>"
+    pool.close()
