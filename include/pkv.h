@@ -75,6 +75,7 @@ extern "C" {
                                  NULL pointer, metadata-only pool)          */
 #define PKV_ERR_DEVICE 7      /* a HIP runtime call failed                  */
 #define PKV_ERR_UNSUPPORTED 8 /* shape outside what the kernels handle      */
+#define PKV_ERR_STATE 9       /* a debug state check failed (pkv_pool_set_checks) */
 
 typedef struct pkv_pool pkv_pool;
 typedef struct pkv_rope pkv_rope;
@@ -117,6 +118,26 @@ void pkv_pool_free(pkv_pool *pool);
  * ("nx_paged_kv_gate.nx source", KAT part: ids 0,1,2 then -1 on a pool of 3;
  * a released id is handed out again.) */
 int64_t pkv_alloc_block(pkv_pool *pool);
+
+/* Debug state checks before device work, for hunting a corrupted pool
+ * (they cost host time; off by default).  level 0: none.  level 1: before
+ * every pkv_ensure_append copy launch, pkv_append_layer and attention call
+ * (metadata-only pools included, for pkv_ensure_append and
+ * pkv_append_layer), the host state the launch relies on: every page id of
+ * the batch's rows in range, each block's reference count at least the
+ * page-table entries naming it (which are at least one), every block new rows
+ * land in held by its sequence alone, copy-on-append targets fresh; and the
+ * batch's row descriptors and pending page-table patches, as built for the
+ * device, against the host page tables and lengths.  level 2: also, before
+ * each attention launch, the device page-table mirror rows of the batch are
+ * read back (synchronizing the stream) and compared with the host page
+ * tables.  A failed check returns PKV_ERR_STATE and launches nothing for
+ * that call (host metadata a pkv_ensure_append has already changed stays
+ * changed: a failure means the state was inconsistent).  PKV_ERR_BAD_ARG for
+ * a level outside 0..2.  (The invariants are those of
+ * "nx_paged_kv_gate.nx source": reference counts that follow the page tables
+ * through fork, copy-on-append and truncate.) */
+int32_t pkv_pool_set_checks(pkv_pool *pool, int32_t level);
 
 /* Give back a reference taken by pkv_alloc_block; at zero the id returns to
  * the free stack, from which the most recently released id is taken first

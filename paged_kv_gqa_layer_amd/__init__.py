@@ -18,12 +18,12 @@ import numpy as np
 from . import _lib
 from ._lib import (BAD_ARG, BAD_DIM, BAD_GQA, CAPACITY, DEVICE, ERR_SEQ,
                    K_APPEND, K_COW, K_DECODE, K_MERGE, K_PREFILL, K_PREFIX,
-                   K_VERIFY, OK, OOM, SIZE_MAX, UNSUPPORTED, Contig, PKVError)
+                   K_VERIFY, OK, OOM, SIZE_MAX, STATE, UNSUPPORTED, Contig, PKVError)
 
 __all__ = [
     "Pool", "ContigCache", "Rope", "PKVError", "lib", "pool_storage_bytes",
     "OK", "BAD_DIM", "BAD_GQA", "ERR_SEQ", "OOM", "CAPACITY", "BAD_ARG",
-    "DEVICE", "UNSUPPORTED", "K_APPEND", "K_DECODE", "K_MERGE", "K_PREFILL",
+    "DEVICE", "UNSUPPORTED", "STATE", "K_APPEND", "K_DECODE", "K_MERGE", "K_PREFILL",
     "K_COW", "K_VERIFY", "K_PREFIX",
 ]
 
@@ -154,6 +154,12 @@ class Pool:
         if rc == OK:
             self.rope = rope
         return rc
+
+    def set_checks(self, level, check=True):
+        """Debug state checks before device work (0 off, 1 host state and row
+        descriptors, 2 also the device page-table mirror)."""
+        return _check(lib().pkv_pool_set_checks(self._h, int(level)), "pool_set_checks",
+                      check)
 
     def close(self):
         if getattr(self, "_h", None):

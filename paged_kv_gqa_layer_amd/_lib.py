@@ -20,6 +20,7 @@ CAPACITY = 5
 BAD_ARG = 6
 DEVICE = 7
 UNSUPPORTED = 8
+STATE = 9
 
 K_APPEND, K_DECODE, K_MERGE, K_PREFILL, K_COW, K_VERIFY, K_PREFIX = range(7)
 
@@ -45,6 +46,7 @@ SIGNATURES = {
     "pkv_rope_new": (_P, [_I32, C.c_double, _I32]),
     "pkv_rope_free": (None, [_P]),
     "pkv_pool_set_rope": (_I32, [_P, _P]),
+    "pkv_pool_set_checks": (_I32, [_P, _I32]),
     "pkv_alloc_block": (_I64, [_P]),
     "pkv_unref_block": (_I32, [_P, _I64]),
     "pkv_pool_set_free_order": (_I32, [_P, _P, _I32]),

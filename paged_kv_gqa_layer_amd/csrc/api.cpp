@@ -493,6 +493,7 @@ struct pkv_pool {
   size_t patch_off = 0;  // patches follow the rows in the blob
   std::unordered_set<int64_t> seen;
   const pkv_rope* rope = nullptr;  // borrowed; null = no rotary embedding
+  int32_t checks = 0;              // debug state checks (pkv_pool_set_checks)
   bool last_shared = false;        // the last attention call grouped prefixes
   int32_t shared_heads = 0;        // ... with this many query heads per kv head
   SharedPlan shared;
@@ -640,6 +641,80 @@ PagedMap make_paged_map(const pkv_pool* p, int32_t layer) {
   pm.v_off = G * B * D;
   pm.block_size = m.block_size();
   return pm;
+}
+
+// Debug state checks (pkv_pool_set_checks).  Host state a launch for the
+// rows of `seqs` relies on: the pages covering seq_len + n rows exist, every
+// page id is in range, each block's count is at least the page-table entries
+// naming it (and those are at least one), and with `writes` every page the
+// n new rows land in is held by this sequence alone.
+int32_t check_state(const pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
+                    bool writes) {
+  const auto& m = p->meta;
+  const auto& ref = m.refcounts();
+  const auto& held = m.holders();
+  const int32_t B = m.block_size();
+  for (int32_t r = 0; r < M; ++r) {
+    const pkv::SeqMeta* q = m.seq(seqs[r]);
+    const int64_t end = static_cast<int64_t>(q->seq_len) + n;
+    if (end > static_cast<int64_t>(q->pages.size()) * B) return PKV_ERR_STATE;
+    for (size_t i = 0; i < q->pages.size(); ++i) {
+      const int32_t b = q->pages[i];
+      if (b < 0 || b >= m.n_blocks() || held[b] < 1 || ref[b] < held[b]) return PKV_ERR_STATE;
+      const int64_t first = static_cast<int64_t>(i) * B;
+      if (writes && first + B > q->seq_len && first < end && ref[b] != 1) return PKV_ERR_STATE;
+    }
+  }
+  return PKV_OK;
+}
+
+// The row blob as built for `seqs` (n rows each) against the host state:
+// every row descriptor names its sequence's length, mirror offset and append
+// block; every page-table patch addresses an entry inside the mirror and a
+// block in range, and a live sequence's patch carries the block its page
+// table holds now.
+int32_t check_blob(const pkv_pool* p, const int32_t* seqs, int32_t M,
+                   const std::vector<int32_t>& blob, size_t patch_off) {
+  const auto& m = p->meta;
+  const int32_t B = m.block_size();
+  if (blob.size() < static_cast<size_t>(M) * pkv::kRowInts || patch_off > blob.size() ||
+      (blob.size() - patch_off) % 3 != 0)
+    return PKV_ERR_STATE;
+  for (int32_t r = 0; r < M; ++r) {
+    const pkv::SeqMeta* q = m.seq(seqs[r]);
+    const int32_t* d = blob.data() + static_cast<size_t>(r) * pkv::kRowInts;
+    const size_t pg = static_cast<size_t>(q->seq_len / B);
+    const int32_t ab = pg < q->pages.size() ? q->pages[pg] : -1;
+    if (d[0] != q->seq_len || d[1] != seqs[r] * p->stride || d[6] != ab) return PKV_ERR_STATE;
+  }
+  for (size_t i = patch_off; i < blob.size(); i += 3) {
+    const int32_t s = blob[i], page = blob[i + 1], b = blob[i + 2];
+    if (s < 0 || s >= m.max_seqs() || page < 0 || page >= p->stride || b < 0 ||
+        b >= m.n_blocks())
+      return PKV_ERR_STATE;
+    const pkv::SeqMeta* q = m.seq(s);
+    if (q && static_cast<size_t>(page) < q->pages.size() && q->pages[page] != b)
+      return PKV_ERR_STATE;
+  }
+  return PKV_OK;
+}
+
+// The device page-table mirror rows of the batch against the host page
+// tables (synchronizes the stream: the pending patches have been applied by
+// the launches enqueued so far).
+int32_t check_mirror(const pkv_pool* p, const int32_t* seqs, int32_t M, hipStream_t st) {
+  if (hipStreamSynchronize(st) != hipSuccess) return PKV_ERR_DEVICE;
+  std::vector<int32_t> row;
+  for (int32_t r = 0; r < M; ++r) {
+    const pkv::SeqMeta* q = p->meta.seq(seqs[r]);
+    row.resize(q->pages.size());
+    if (row.empty()) continue;
+    if (hipMemcpy(row.data(), p->mirror + static_cast<int64_t>(seqs[r]) * p->stride,
+                  row.size() * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess)
+      return PKV_ERR_DEVICE;
+    if (row != q->pages) return PKV_ERR_STATE;
+  }
+  return PKV_OK;
 }
 
 bool contig_valid(const pkv_contig* c) {
@@ -810,6 +885,7 @@ const char* pkv_strerror(int32_t code) {
     case PKV_ERR_BAD_ARG: return "bad argument";
     case PKV_ERR_DEVICE: return "HIP runtime error";
     case PKV_ERR_UNSUPPORTED: return "unsupported shape";
+    case PKV_ERR_STATE: return "pool state check failed";
     default: return "unknown status";
   }
 }
@@ -889,6 +965,13 @@ pkv_rope* pkv_rope_new(int32_t head_dim, double log_base,
 
 void pkv_rope_free(pkv_rope* rope) { delete rope; }
 
+int32_t pkv_pool_set_checks(pkv_pool* pool, int32_t level) {
+  if (!pool) return PKV_ERR_BAD_ARG;
+  if (level < 0 || level > 2) return PKV_ERR_BAD_ARG;
+  pool->checks = level;
+  return PKV_OK;
+}
+
 int32_t pkv_pool_set_rope(pkv_pool* pool, const pkv_rope* rope) {
   if (!pool) return PKV_ERR_BAD_ARG;
   if (rope && rope->head_dim != pool->meta.head_dim()) return PKV_ERR_BAD_DIM;
@@ -936,7 +1019,16 @@ int32_t pkv_ensure_append(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (!pool) return PKV_ERR_BAD_ARG;
   std::vector<pkv::CowCopy> cows;
   const int32_t rc = pool->meta.ensure_append(seqs, M, n_new, &cows);
-  if (rc != PKV_OK || cows.empty() || !pool->storage) return rc;
+  if (rc != PKV_OK) return rc;
+  if (pool->checks > 0) {
+    if (int32_t c = check_state(pool, seqs, M, n_new, true)) return c;
+    for (const auto& c : cows)
+      if (c.src < 0 || c.src >= pool->meta.n_blocks() || c.dst < 0 ||
+          c.dst >= pool->meta.n_blocks() || pool->meta.refcounts()[c.dst] != 1 ||
+          pool->meta.refcounts()[c.src] < 1)
+        return PKV_ERR_STATE;
+  }
+  if (cows.empty() || !pool->storage) return rc;
   // copy the privatised blocks on the stream, before any append
   const hipStream_t st = as_stream(stream);
   if (pool->dev.use_stream(st) != hipSuccess) return PKV_ERR_DEVICE;
@@ -964,6 +1056,8 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (layer < 0 || layer >= pool->meta.n_layers()) return PKV_ERR_BAD_ARG;
   if (int32_t rc = pool->meta.check_append(seqs, M, n_new)) return rc;
   if (int32_t rc = pool_rope_check(pool, seqs, M, n_new)) return rc;
+  if (pool->checks > 0)
+    if (int32_t rc = check_state(pool, seqs, M, n_new, true)) return rc;
   if (!pool->storage) return PKV_OK;  // metadata-only pool: checks only
   if (!K_new_dev || !V_new_dev) return PKV_ERR_BAD_ARG;
   const hipStream_t st = as_stream(stream);
@@ -980,6 +1074,8 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   if (pool_rows(pool, seqs, M, n_new, shared_heads, st, &rows,
                 n_new == 1 ? &pa : nullptr) != hipSuccess)
     return PKV_ERR_DEVICE;
+  if (pool->checks > 0)
+    if (int32_t rc = check_blob(pool, seqs, M, pool->rows, pool->patch_off)) return rc;
   const PagedMap pm = make_paged_map(pool, layer);
   const int32_t kv_dim = pool->meta.n_kv_heads() * pool->meta.head_dim();
   const int32_t span = pool->rope ? pool->meta.head_dim() / 2 : pool->meta.head_dim();
@@ -1077,8 +1173,14 @@ int32_t paged_attention(pkv_pool* pool, const int32_t* seqs, int32_t M,
     pool->last_shared = sh > 0;
     pool->shared_heads = sh;
   }
+  if (pool->checks > 0)
+    if (int32_t rc = check_state(pool, seqs, M, n_q, false)) return rc;
   const int32_t* rows = nullptr;
   if (pool_rows(pool, seqs, M, n_q, sh, st, &rows) != hipSuccess) return PKV_ERR_DEVICE;
+  if (pool->checks > 0)
+    if (int32_t rc = check_blob(pool, seqs, M, pool->rows, pool->patch_off)) return rc;
+  if (pool->checks > 1)
+    if (int32_t rc = check_mirror(pool, seqs, M, st)) return rc;
   const PagedMap pm = make_paged_map(pool, layer);
   return run_attention(pool->dev, pm, rows, pool->plan, Q_dev, out_dev, ws_dev,
                        n_heads, n_kv_heads, head_dim, n_q, causal, scale, M,
@@ -1166,9 +1268,13 @@ int32_t pkv_attn_paged_decode_noalloc(pkv_pool* pool, const int32_t* seqs, int32
   // growing the page-table mirror would allocate
   if (!pool->mirror || pkv::PoolMeta::mirror_stride(m.max_pages_seen()) > pool->stride)
     return PKV_ERR_UNSUPPORTED;
+  if (pool->checks > 0)
+    if (int32_t rc = check_state(pool, seqs, M, 1, false)) return rc;
   RowPlan plan;
   size_t patch_off = 0;
   build_blob(pool, seqs, M, 1, 0, pool->na_rows, &plan, &patch_off);
+  if (pool->checks > 0)
+    if (int32_t rc = check_blob(pool, seqs, M, pool->na_rows, patch_off)) return rc;
   const int32_t group = n_heads / n_kv_heads;
   const size_t part = uses_splits(Kind::kDecode, head_dim, group, m.block_size(), 1)
                           ? partial_bytes(plan, 1, n_heads, head_dim)
@@ -1192,6 +1298,8 @@ int32_t pkv_attn_paged_decode_noalloc(pkv_pool* pool, const int32_t* seqs, int32
       return PKV_ERR_DEVICE;
     m.patches().clear();
   }
+  if (pool->checks > 1)
+    if (int32_t rc = check_mirror(pool, seqs, M, st)) return rc;
   pool->last_shared = false;
   pool->shared_heads = 0;
   pool->dev.no_new_events = true;

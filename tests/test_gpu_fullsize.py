@@ -1,8 +1,13 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times: sampled outputs against the oracle (one sequence / query at
-a time), properties on every output, pool state against the oracle's, and
-the fork / rewind invariants bit for bit.  Decode, verify (4 and 8 drafted
-rows with rewind), prefill and the forked workload."""
+benchmark times: outputs against the oracle (one sequence / query per oracle
+call, spread over the host cores), properties on every output, pool state
+against the oracle's, and the fork / rewind invariants bit for bit.  Decode
+(every row of the M=256 step), verify (4 and 8 drafted rows with rewind),
+prefill (every 16th query and the tile edges of all 8 sequences) and the
+forked workload (every fork at four steps)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +21,17 @@ from pkv_gpu import assert_close, bits_equal, dev
 pytestmark = pytest.mark.gpu
 
 
+def _workers():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return max(1, min(16, n))
+
+
+def _parallel(fn, jobs):
+    """fn over jobs on the host cores (the oracle runs outside the GIL)."""
+    with ThreadPoolExecutor(max_workers=_workers()) as ex:
+        return list(ex.map(fn, jobs))
+
+
 def _pool_for(wl, n_layers=1, max_seqs=None):
     pool = pkv.Pool(wl.n_blocks, wl.block_size, n_layers, wl.n_kv_heads,
                     wl.head_dim, max_seqs=max_seqs or wl.M + 8)
@@ -23,7 +39,8 @@ def _pool_for(wl, n_layers=1, max_seqs=None):
     return pool
 
 
-def test_decode_m256_full_size_sampled_rows():
+def test_decode_m256_full_size_every_row():
+    """Every row of a decode step of the M=256 workload against the oracle."""
     wl = synth.decode_m256(max_steps=2)
     H, G, D, M = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.M
     pool = _pool_for(wl)
@@ -45,14 +62,16 @@ def test_decode_m256_full_size_sampled_rows():
     assert np.all(np.isfinite(got))
     # |out| is a convex combination of N(0,1) values: loose sanity bound
     assert np.abs(got).max() < 10
-    rows = sorted({int(np.argmin(wl.ctx)), int(np.argmax(wl.ctx)), 0, 1, 77, 128, 255})
-    for r in rows:
+
+    def check(r):
         kh, vh = wl.history(r)
         rc, ref = oracle.attn_contig(q[r:r + 1], np.concatenate([kh, k[r:r + 1]]),
                                      np.concatenate([vh, v[r:r + 1]]), H, G, D, True,
                                      wl.scale)
         assert rc == 0
         assert_close(got[r:r + 1], ref, "m256 row %d (ctx %d)" % (r, wl.ctx[r]))
+        return r
+    assert _parallel(check, range(M)) == list(range(M))
     pool.advance(seqs_np, 1, check=True)
     pool.close()
 
@@ -73,7 +92,8 @@ def test_verify_m256_full_size_sampled_rows_with_rewind():
     gen = np.random.default_rng(41)
     kept = [np.zeros((0, G * D), np.float32) for _ in range(M)]
     kept_v = [np.zeros((0, G * D), np.float32) for _ in range(M)]
-    rows = sorted({int(np.argmin(wl.ctx)), int(np.argmax(wl.ctx)), 0, 1, 77, 128, 255})
+    rows = sorted({int(np.argmin(wl.ctx)), int(np.argmax(wl.ctx)), 1, 77, 255} |
+                  set(range(0, M, 8)))
     for n_q in (4, 8):
         q = gen.standard_normal((M * n_q, H * D), dtype=np.float32)
         k = gen.standard_normal((M * n_q, G * D), dtype=np.float32)
@@ -90,7 +110,8 @@ def test_verify_m256_full_size_sampled_rows_with_rewind():
         got = out.cpu().numpy()
         assert np.all(np.isfinite(got))
         assert np.abs(got).max() < 10
-        for r in rows:
+
+        def check(r):
             kh, vh = wl.history(r)
             sl = slice(r * n_q, (r + 1) * n_q)
             rc, ref = oracle.attn_contig(q[sl], np.concatenate([kh, kept[r], k[sl]]),
@@ -98,6 +119,8 @@ def test_verify_m256_full_size_sampled_rows_with_rewind():
                                          True, wl.scale)
             assert rc == 0
             assert_close(got[sl], ref, "verify n_q %d row %d (ctx %d)" % (n_q, r, wl.ctx[r]))
+            return r
+        assert _parallel(check, rows) == rows
         # keep a seeded 1..n_q of the drafted rows, rewind the rest
         accept = gen.integers(1, n_q + 1, size=M)
         for r, s in enumerate(seqs):
@@ -109,7 +132,9 @@ def test_verify_m256_full_size_sampled_rows_with_rewind():
     pool.close()
 
 
-def test_prefill_full_size_sampled_queries():
+def test_prefill_full_size_every_16th_query():
+    """Every 16th chunk query and the tile-edge queries of all 8 sequences of
+    the 8 x (3584 + 512) prefill against the oracle."""
     wl = synth.prefill_8x3584p512()
     H, G, D, M, n_q = wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.M, wl.chunk
     pool = _pool_for(wl)
@@ -130,17 +155,26 @@ def test_prefill_full_size_sampled_queries():
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
-    for r in (0, 5, 7):
+    queries = sorted(set(range(0, n_q, 16)) |
+                     {1, 31, 32, 33, 63, 64, 127, 128, 255, 256, 480, 510, 511})
+
+    # one sequence per worker would leave most host cores idle: split the
+    # query list of each sequence four ways
+    parts = [(r, queries[j::4]) for r in range(M) for j in range(4)]
+
+    def check_part(job):
+        r, qs = job
         kh, vh = wl.history(r)
         Kall = np.concatenate([kh, chunks[r][1]])
         Vall = np.concatenate([vh, chunks[r][2]])
-        for i in (0, 1, 31, 32, 33, 127, 255, 256, 480, 510, 511):
-            # query i sees keys 0..cached+i: the same as one query over that prefix
+        for i in qs:
             nk = wl.cached + i + 1
             rc, ref = oracle.attn_contig(chunks[r][0][i:i + 1], Kall[:nk], Vall[:nk],
                                          H, G, D, True, wl.scale)
             assert rc == 0
             assert_close(got[r * n_q + i:r * n_q + i + 1], ref, "seq %d query %d" % (r, i))
+        return len(qs)
+    assert sum(_parallel(check_part, parts)) == M * len(queries)
     pool.close()
 
 
@@ -212,15 +246,20 @@ def test_forked_prefix_decode_and_rewind(prefix, n_forks, steps):
         tails = {int(pool.seq_pages(f)[prefix // wl.block_size]) for f in forks}
         assert len(tails) == n_forks and all(ref[b] == 1 for b in tails)
 
-    # oracle on sampled (fork, step) outputs
-    for f in (0, n_forks - 1):
-        for t in sorted({0, steps // 2, steps - 1}):
+    # every fork against the oracle at four steps (first, two inner, last)
+    check_steps = sorted({0, steps // 3, (2 * steps) // 3, steps - 1})
+    got = {t: outs[t].cpu().numpy() for t in check_steps}
+
+    def check(f):
+        for t in check_steps:
             kk = np.concatenate([pk] + [steps_in[s][f][1][None] for s in range(t + 1)])
             vv = np.concatenate([pv] + [steps_in[s][f][2][None] for s in range(t + 1)])
             rc, r_ = oracle.attn_contig(steps_in[t][f][0][None], kk, vv, H, G, D, True,
                                         wl.scale)
             assert rc == 0
-            assert_close(outs[t][f:f + 1].cpu().numpy(), r_, "fork %d step %d" % (f, t))
+            assert_close(got[t][f:f + 1], r_, "fork %d step %d" % (f, t))
+        return f
+    assert _parallel(check, range(n_forks)) == list(range(n_forks))
 
     # rewind: even forks go back to the fork point and replay their odd
     # partner's stream; every output must equal the partner's bit for bit

@@ -161,6 +161,9 @@ def test_random_ops_state_matches_oracle(seed):
     max_seqs = 6
     o = oracle.Pool(n_blocks, B, 2, 1, 2, max_seqs=max_seqs, with_storage=False)
     p = pkv.Pool(n_blocks, B, 2, 1, 2, max_seqs=max_seqs, device=None)
+    # odd seeds run with the debug state checks on: they must never fire on
+    # states the operations produce, nor change any status
+    p.set_checks(seed % 2)
     perm = rng.permutation(n_blocks)
     assert o.set_free_order(perm) == p.set_free_order(perm, check=False) == 0
     raw = []
@@ -318,3 +321,12 @@ def test_split_plan_sizes(n_q):
         assert ws([seq_len]) == (k * per_slot if k > 1 else 0), seq_len
     assert ws(edges) == sum(slots) * per_slot
     assert ws(edges[::-1]) == sum(slots) * per_slot
+
+
+def test_set_checks_arguments():
+    p = pkv.Pool(8, 4, 1, 1, 4, device=None)
+    assert p.set_checks(0) == 0 and p.set_checks(2) == 0
+    assert p.set_checks(3, check=False) == pkv.BAD_ARG
+    assert p.set_checks(-1, check=False) == pkv.BAD_ARG
+    assert pkv.lib().pkv_pool_set_checks(None, 1) == pkv.BAD_ARG
+    assert pkv.lib().pkv_strerror(pkv.STATE) == b"pool state check failed"
