@@ -339,6 +339,23 @@ int32_t pkv_attn_with_paged_decode(pkv_pool *pool, const int32_t *seqs,
                                    float *out_dev, void *ws_dev,
                                    size_t ws_bytes, void *stream);
 
+/* pkv_attn_with_paged_decode for pkv_attn_paged_decode_shared: after the
+ * checks of both calls, pkv_append_layer of one row per sequence, then the
+ * shared-prefix decode (the same launches, so the same pool bytes and
+ * output bits).  ws_dev: >= pkv_decode_shared_workspace_bytes bytes.
+ * Errors as
+ * pkv_attn_with_paged_decode.  ("nx_f32_attn_paged.nx source":
+ * nx_f32_attn_with_paged, with the fork sharing of "nx_paged_kv_gate.nx
+ * source".) */
+int32_t pkv_attn_with_paged_decode_shared(pkv_pool *pool, const int32_t *seqs,
+                                          int32_t M, int32_t layer,
+                                          int32_t n_heads, int32_t n_kv_heads,
+                                          int32_t head_dim, const float *Q_dev,
+                                          const float *K_new_dev,
+                                          const float *V_new_dev, float scale,
+                                          float *out_dev, void *ws_dev,
+                                          size_t ws_bytes, void *stream);
+
 /* Device workspace bytes pkv_attn_paged_decode_shared needs for this batch
  * (prefix and split partial results); 0 if none, (size_t)-1 on bad
  * arguments. */

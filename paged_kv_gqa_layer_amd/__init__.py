@@ -265,6 +265,24 @@ class Pool:
             self._h, _vp(a), a.size, layer, n_heads, n_kv_heads, head_dim, qp, kp, vp,
             float(scale), op, wp, wb, _stream(stream)), "attn_with_paged_decode", check)
 
+    def attn_with_paged_decode_shared(self, seqs, layer, n_heads, n_kv_heads, head_dim,
+                                      Q, K_new, V_new, scale, out, ws=None, stream=None,
+                                      check=False):
+        """append_layer of one row per sequence, then
+        attn_paged_decode_shared, as one call."""
+        a = _ids(seqs)
+        q_dim = n_heads * head_dim
+        kv_dim = n_kv_heads * head_dim
+        qp = _dptr(Q, "Q", a.size * q_dim)
+        kp = _dptr(K_new, "K_new", a.size * kv_dim)
+        vp = _dptr(V_new, "V_new", a.size * kv_dim)
+        op = _dptr(out, "out", a.size * q_dim)
+        wp, wb = _ws(ws)
+        return _check(lib().pkv_attn_with_paged_decode_shared(
+            self._h, _vp(a), a.size, layer, n_heads, n_kv_heads, head_dim, qp, kp, vp,
+            float(scale), op, wp, wb, _stream(stream)), "attn_with_paged_decode_shared",
+            check)
+
     def decode_shared_workspace_bytes(self, seqs, n_heads):
         a = _ids(seqs)
         return lib().pkv_decode_shared_workspace_bytes(self._h, _vp(a), a.size, n_heads)

@@ -66,6 +66,8 @@ SIGNATURES = {
                                           _P, _P, _P, _F, _P, _P, _SZ, _P]),
     "pkv_attn_paged_prefill": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32,
                                       _I32, _P, _I32, _F, _P, _P]),
+    "pkv_attn_with_paged_decode_shared": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32,
+                                                 _P, _P, _P, _F, _P, _P, _SZ, _P]),
     "pkv_decode_shared_workspace_bytes": (_SZ, [_P, _P, _I32, _I32]),
     "pkv_attn_paged_decode_shared": (_I32, [_P, _P, _I32, _I32, _I32, _I32, _I32,
                                             _P, _F, _P, _P, _SZ, _P]),

@@ -1224,14 +1224,16 @@ int32_t pkv_attn_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
                          stream);
 }
 
-int32_t pkv_attn_with_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
-                                   int32_t layer, int32_t n_heads, int32_t n_kv_heads,
-                                   int32_t head_dim, const float* Q_dev,
-                                   const float* K_new_dev, const float* V_new_dev,
-                                   float scale, float* out_dev, void* ws_dev,
-                                   size_t ws_bytes, void* stream) {
-  // every check of both calls first, in the pages' order, so an error
-  // leaves the pool as it was
+namespace {
+
+// pkv_attn_with_paged_decode and its shared-prefix form: every check of
+// both calls first, in the pages' order, so an error leaves the pool as it
+// was; then append_layer's launch and the attention's.
+int32_t with_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M, int32_t layer,
+                          int32_t n_heads, int32_t n_kv_heads, int32_t head_dim,
+                          const float* Q_dev, const float* K_new_dev, const float* V_new_dev,
+                          float scale, float* out_dev, void* ws_dev, size_t ws_bytes,
+                          Kind kind, void* stream) {
   if (!pool) return PKV_ERR_BAD_ARG;
   if (int32_t rc = attn_front_checks(M, 1, n_heads, n_kv_heads, head_dim)) return rc;
   const auto& m = pool->meta;
@@ -1242,12 +1244,37 @@ int32_t pkv_attn_with_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t 
   if (int32_t rc = pool_rope_check(pool, seqs, M, 1)) return rc;
   if (!pool->storage) return PKV_ERR_BAD_ARG;
   if (!Q_dev || !out_dev || !K_new_dev || !V_new_dev) return PKV_ERR_BAD_ARG;
-  const size_t need = pool_workspace_bytes(pool, seqs, M, 1, n_heads, Kind::kDecode);
+  const size_t need = pool_workspace_bytes(pool, seqs, M, 1, n_heads, kind);
   if (need > 0 && (!ws_dev || ws_bytes < need)) return PKV_ERR_BAD_ARG;
   if (int32_t rc = pkv_append_layer(pool, seqs, M, 1, layer, K_new_dev, V_new_dev, stream))
     return rc;
-  return pkv_attn_paged_decode(pool, seqs, M, layer, n_heads, n_kv_heads, head_dim, Q_dev,
-                               scale, out_dev, ws_dev, ws_bytes, stream);
+  return paged_attention(pool, seqs, M, 1, layer, n_heads, n_kv_heads, head_dim, Q_dev, 1,
+                         scale, out_dev, ws_dev, ws_bytes, kind, stream);
+}
+
+}  // namespace
+
+int32_t pkv_attn_with_paged_decode(pkv_pool* pool, const int32_t* seqs, int32_t M,
+                                   int32_t layer, int32_t n_heads, int32_t n_kv_heads,
+                                   int32_t head_dim, const float* Q_dev,
+                                   const float* K_new_dev, const float* V_new_dev,
+                                   float scale, float* out_dev, void* ws_dev,
+                                   size_t ws_bytes, void* stream) {
+  return with_paged_decode(pool, seqs, M, layer, n_heads, n_kv_heads, head_dim, Q_dev,
+                           K_new_dev, V_new_dev, scale, out_dev, ws_dev, ws_bytes,
+                           Kind::kDecode, stream);
+}
+
+int32_t pkv_attn_with_paged_decode_shared(pkv_pool* pool, const int32_t* seqs, int32_t M,
+                                          int32_t layer, int32_t n_heads,
+                                          int32_t n_kv_heads, int32_t head_dim,
+                                          const float* Q_dev, const float* K_new_dev,
+                                          const float* V_new_dev, float scale,
+                                          float* out_dev, void* ws_dev, size_t ws_bytes,
+                                          void* stream) {
+  return with_paged_decode(pool, seqs, M, layer, n_heads, n_kv_heads, head_dim, Q_dev,
+                           K_new_dev, V_new_dev, scale, out_dev, ws_dev, ws_bytes,
+                           Kind::kDecodeShared, stream);
 }
 
 int32_t pkv_attn_paged_decode_noalloc(pkv_pool* pool, const int32_t* seqs, int32_t M,

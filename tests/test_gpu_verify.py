@@ -47,6 +47,12 @@ def _rand(rng, shape, sigma=1.0):
     (16, 8, 8),    # group 2: 16 rows, one MFMA block
     (64, 8, 4),    # group 8: 32 rows, two blocks
     (64, 8, 5),    # 40 rows: runs the prefill kernels
+    # groups the decode kernel does not take but the split multi-query kernel
+    # does (n_q x group <= 32): group 3 and group 16
+    (24, 8, 1), (24, 8, 2), (24, 8, 5), (24, 8, 8), (24, 8, 10),
+    (24, 8, 11),   # 33 rows: the generic kernel
+    (32, 2, 1), (32, 2, 2),
+    (32, 2, 3),    # 48 rows: the generic kernel
 ])
 def test_verify_vs_oracle_and_contiguous(H, G, n_q):
     D = 128
