@@ -1049,6 +1049,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 // each member's new row) and each row's unnormalised state goes to its
 // prefix partial slot for merge_kernel.
 constexpr int kPfKT = 32;     // keys per tile
+constexpr float kLazyMax = 8.f;  // lazy-rescale threshold (base-2 score units)
 constexpr int kPfKSTR = 132;  // padded LDS row strides (bank spread)
 constexpr int kPfVSTR = 136;
 // two K/V tile buffers: tile t+1 is stored while tile t is read
@@ -1223,13 +1224,31 @@ __device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
     const int32_t k0 = t * KT;
     if (k0 < w_lim) {
       floatx16 S = {};
+      if constexpr (PREFIX) {
+        // one workgroup per CU here (one wave per SIMD): two independent
+        // accumulation chains (even / odd dims of each group of four),
+        // summed at the end, so the matrix pipe never waits on the
+        // previous MFMA's result
+        floatx16 S2 = {};
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const float4 kf = *reinterpret_cast<const float4*>(&Ks[lr * KSTR + 8 * u + 4 * h]);
-        S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x, qreg[u].x, S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.y, qreg[u].y, S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.z, qreg[u].z, S, 0, 0, 0);
-        S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qreg[u].w, S, 0, 0, 0);
+        for (int u = 0; u < 16; ++u) {
+          const float4 kf = *reinterpret_cast<const float4*>(&Ks[lr * KSTR + 8 * u + 4 * h]);
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x, qreg[u].x, S, 0, 0, 0);
+          S2 = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.y, qreg[u].y, S2, 0, 0, 0);
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.z, qreg[u].z, S, 0, 0, 0);
+          S2 = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qreg[u].w, S2, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[r] += S2[r];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const float4 kf = *reinterpret_cast<const float4*>(&Ks[lr * KSTR + 8 * u + 4 * h]);
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.x, qreg[u].x, S, 0, 0, 0);
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.y, qreg[u].y, S, 0, 0, 0);
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.z, qreg[u].z, S, 0, 0, 0);
+          S = __builtin_amdgcn_mfma_f32_32x32x2f32(kf.w, qreg[u].w, S, 0, 0, 0);
+        }
       }
       // mask and row max: this lane holds row lr, keys k0 + 8*(r/4) + 4*h + r%4
       float mx = kNegInf;
@@ -1245,28 +1264,39 @@ __device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
           mx = fmaxf(mx, S[r]);
         }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // finite: every row sees key k_first (causal rows see key 0 onwards)
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - m_new);
+      // Lazy rescale: the reference maximum m_run of a row moves only when
+      // a score exceeds it by more than kLazyMax (base-2 units); below that
+      // the tile's weights are taken against the old reference (each at
+      // most 2^kLazyMax).  O and l share the reference, so O / l is the
+      // softmax-weighted sum either way.  The test is wave-uniform; in it
+      // the two lanes of a row (h = 0, 1) agree on the row maximum.  The
+      // first tile always moves it (m_run starts at -inf and every row
+      // sees a key of its first tile: causal rows see key 0 onwards).
+      if (__ballot(mx > m_run + kLazyMax)) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+        // every O^T block keeps row lr in this lane: the rescale is
+        // lane-local
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          O0[r] *= alpha;
+          O1[r] *= alpha;
+          O2[r] *= alpha;
+          O3[r] *= alpha;
+        }
+      }
+      // this lane's keys only: the two halves of a row's sum are added once,
+      // after the last tile
       float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        S[r] = fast_exp2(S[r] - m_new);
+        S[r] = fast_exp2(S[r] - m_run);
         ps += S[r];
       }
-      ps += __shfl_xor(ps, 32);
-      l_run = fmaf(l_run, alpha, ps);
-      m_run = m_new;
-      // O^T block b (dims 32b ..) keeps row lr in this lane: the rescale is
-      // lane-local
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        O0[r] *= alpha;
-        O1[r] *= alpha;
-        O2[r] *= alpha;
-        O3[r] *= alpha;
-      }
+      l_run += ps;
       // O^T = V^T P^T: A = V^T (lane: dim 32b + lr, key of step s), B = P^T
       // (lane: row lr, the same key -- score accumulator s)
 #pragma unroll
@@ -1288,6 +1318,7 @@ __device__ __forceinline__ void prefill_block(const Map& m, const AttnArgs& a,
   // Store: this lane holds row lr (query or member, head jh); accumulator r
   // of block b is dim 32b + 8(r/4) + 4h + r%4.  Prefill divides by the row
   // sum; the prefix form writes the unnormalised state of its key range.
+  l_run += __shfl_xor(l_run, 32);
   if (!row_valid) return;
   const int64_t e = PREFIX ? slot * a.n_heads + kvh * GROUP + jh
                            : (int64_t)q_row * a.n_heads + kvh * GROUP + jh;
