@@ -57,9 +57,19 @@ struct DeviceCtx {
     void* host = nullptr;
     const void* dev = nullptr;  // the same memory as kernels address it
     size_t cap = 0;
-    hipEvent_t ev = nullptr;
-    bool pending = false;
+    bool used = false;  // read by an enqueued launch or copy not known done
   };
+  // Slot guard events, one per group of kSlotGroup consecutive slots: the
+  // event of a group is recorded after the launch or copy that reads the
+  // group's last slot, so (the stream being in order) it completes after
+  // every earlier reader of the group's slots; a used slot is rewritten only
+  // after that.  One record per group rather than per use: each record is a
+  // system-scope release in the stream (an L2 write-back before the signal),
+  // several microseconds of GPU time that the next launch waits behind.
+  static constexpr int kSlotGroup = 4;
+  static constexpr int kSlotGroups = kStageSlots / kSlotGroup;
+  hipEvent_t group_ev[kSlotGroups] = {};
+  bool group_rec[kSlotGroups] = {};  // recorded since the group was last freed
   struct DevBuf {
     void* ptr = nullptr;
     size_t cap = 0;
@@ -88,8 +98,12 @@ struct DeviceCtx {
 
   void release() {
     if (used) (void)hipStreamSynchronize(last_stream);
+    for (int g = 0; g < kSlotGroups; ++g) {
+      if (group_ev[g]) (void)hipEventSynchronize(group_ev[g]), (void)hipEventDestroy(group_ev[g]);
+      group_ev[g] = nullptr;
+      group_rec[g] = false;
+    }
     for (auto& s : slot) {
-      if (s.ev) (void)hipEventSynchronize(s.ev), (void)hipEventDestroy(s.ev);
       if (s.host) (void)hipHostFree(s.host);
       s = Slot();
     }
@@ -168,14 +182,21 @@ struct DeviceCtx {
   // with room for `bytes`.
   hipError_t take_slot(size_t bytes, Slot** out) {
     Slot& s = slot[next];
+    const int g = next / kSlotGroup;
     last_slot = next;
     next = (next + 1) % kStageSlots;
     hipError_t e;
-    if (s.pending) {
-      if ((e = hipEventSynchronize(s.ev)) != hipSuccess) return e;
-      s.pending = false;
+    if (s.used) {
+      // the group's event follows every use of its slots; without one (a
+      // reader whose launch failed after the slot was filled) wait for the
+      // whole stream
+      e = group_rec[g] ? hipEventSynchronize(group_ev[g]) : hipStreamSynchronize(last_stream);
+      if (e != hipSuccess) return e;
+      for (int j = g * kSlotGroup; j < (g + 1) * kSlotGroup; ++j) slot[j].used = false;
+      group_rec[g] = false;
     }
-    if (!s.ev && (e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming)) != hipSuccess)
+    if (!group_ev[g] &&
+        (e = hipEventCreateWithFlags(&group_ev[g], hipEventDisableTiming)) != hipSuccess)
       return e;
     if (bytes > s.cap) {
       if (s.host) (void)hipHostFree(s.host);
@@ -217,8 +238,7 @@ struct DeviceCtx {
       if ((e = hipMemcpyAsync(d.ptr, s->host, blob.size() * sizeof(int32_t),
                               hipMemcpyHostToDevice, st)) != hipSuccess)
         return e;
-      if ((e = hipEventRecord(s->ev, st)) != hipSuccess) return e;
-      s->pending = true;
+      if ((e = staged(st)) != hipSuccess) return e;
     }
     d.key = key;
     d.valid = !key.empty();
@@ -253,10 +273,31 @@ struct DeviceCtx {
     *dev = static_cast<int32_t*>(d.ptr);
     return hipSuccess;
   }
+  // Buffer b holds the blob `key` names (an upload of it would copy nothing).
+  bool holds(int b, const std::vector<int64_t>& key) const {
+    return !key.empty() && buf[b].valid && buf[b].key == key;
+  }
+
+  // Device buffer b sized for `bytes` and marked as holding `key`, for a
+  // launch that writes the blob there itself (its argument copy).
+  hipError_t claim(int b, size_t bytes, const std::vector<int64_t>& key, hipStream_t st,
+                   int32_t** dev) {
+    DevBuf& d = buf[b];
+    d.valid = false;
+    const hipError_t e = reserve(b, std::max<size_t>(bytes, 1), st);
+    if (e != hipSuccess) return e;
+    d.key = key;
+    d.valid = !key.empty();
+    *dev = static_cast<int32_t*>(d.ptr);
+    return hipSuccess;
+  }
+
   hipError_t staged(hipStream_t st) {
-    Slot& s = slot[last_slot];
-    const hipError_t e = hipEventRecord(s.ev, st);
-    if (e == hipSuccess) s.pending = true;
+    slot[last_slot].used = true;
+    if (last_slot % kSlotGroup != kSlotGroup - 1) return hipSuccess;
+    const int g = last_slot / kSlotGroup;
+    const hipError_t e = hipEventRecord(group_ev[g], st);
+    if (e == hipSuccess) group_rec[g] = true;
     return e;
   }
 
@@ -574,33 +615,44 @@ void build_blob(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
   }
 }
 
-// Row descriptors of this batch (see build_blob) on the device, with the
-// pending page-table patches applied to the mirror first.  Rows and patches
-// travel in one upload, which is skipped when the device copy already
-// describes this batch at this pool version (no patches can be pending then:
-// every page-table change bumps the version).
+// pool_rows: row descriptors of this batch (see build_blob) on the device,
+// with the pending page-table patches applied to the mirror first.  Rows and
+// patches travel in one upload, which is skipped when the device copy
+// already describes this batch at this pool version (no patches can be
+// pending then: every page-table change bumps the version).
 // With `fused` (the one-row append), both the upload and the patches are
 // left to the caller's kernel: *rows_dev is then the copy that kernel reads
 // (the pinned staging copy when an upload is due), *fused says what it must
 // copy and patch, and the caller calls p->dev.staged(st) after the launch
 // when fused->n_copy > 0.
-hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
-                     int32_t shared_heads, hipStream_t st, const int32_t** rows_dev,
-                     pkv::PatchArgs* fused = nullptr) {
-  hipError_t e = size_mirror(p, st);
+//
+// Its first half: the mirror sized for every sequence and the row blob of
+// this batch in p->rows / p->plan (rebuilt unless the last one already
+// describes this batch at this pool version); *key names it.
+hipError_t plan_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
+                     int32_t shared_heads, hipStream_t st, std::vector<int64_t>* key) {
+  const hipError_t e = size_mirror(p, st);
   if (e != hipSuccess) return e;
-  std::vector<int64_t> key;
-  key.reserve(M + 4);
-  key.push_back(static_cast<int64_t>(p->meta.version()));
-  key.push_back(p->stride);
-  key.push_back(n);
-  key.push_back(shared_heads);
-  key.insert(key.end(), seqs, seqs + M);
-  auto& pt = p->meta.patches();
-  if (key != p->rows_key || !pt.empty()) {
+  key->clear();
+  key->reserve(M + 4);
+  key->push_back(static_cast<int64_t>(p->meta.version()));
+  key->push_back(p->stride);
+  key->push_back(n);
+  key->push_back(shared_heads);
+  key->insert(key->end(), seqs, seqs + M);
+  if (*key != p->rows_key || !p->meta.patches().empty()) {
     build_blob(p, seqs, M, n, shared_heads, p->rows, &p->plan, &p->patch_off);
     p->rows_key.clear();  // the blob below is new
   }
+  return hipSuccess;
+}
+
+// Second half: the blob plan_rows left in p->rows (named by key) to the
+// device.
+hipError_t rows_to_device(pkv_pool* p, const std::vector<int64_t>& key, hipStream_t st,
+                          const int32_t** rows_dev, pkv::PatchArgs* fused) {
+  hipError_t e;
+  auto& pt = p->meta.patches();
   const int32_t n_patch = static_cast<int32_t>((p->rows.size() - p->patch_off) / 3);
   int32_t* d = nullptr;
   if (fused) {
@@ -627,6 +679,21 @@ hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
   p->rows_key = key;
   *rows_dev = d;
   return hipSuccess;
+}
+
+hipError_t pool_rows(pkv_pool* p, const int32_t* seqs, int32_t M, int32_t n,
+                     int32_t shared_heads, hipStream_t st, const int32_t** rows_dev,
+                     pkv::PatchArgs* fused = nullptr) {
+  std::vector<int64_t> key;
+  const hipError_t e = plan_rows(p, seqs, M, n, shared_heads, st, &key);
+  if (e != hipSuccess) return e;
+  return rows_to_device(p, key, st, rows_dev, fused);
+}
+
+// Floats per head unit of the append scatter (half a head with a rotary
+// table: a thread takes a value and its rotation partner).
+int32_t span_of(const pkv_pool* p) {
+  return p->rope ? p->meta.head_dim() / 2 : p->meta.head_dim();
 }
 
 PagedMap make_paged_map(const pkv_pool* p, int32_t layer) {
@@ -1070,17 +1137,53 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
   // one row per sequence: the rows name the blocks they land in, so the
   // append kernel also applies the pending page-table patches and brings
   // the step's row blob to the device
+  std::vector<int64_t> key;
+  if (plan_rows(pool, seqs, M, n_new, shared_heads, st, &key) != hipSuccess)
+    return PKV_ERR_DEVICE;
+  // after plan_rows: sizing the mirror may have moved it
+  const PagedMap pm = make_paged_map(pool, layer);
+  const int32_t kv_dim = pool->meta.n_kv_heads() * pool->meta.head_dim();
+  if (n_new == 1) {
+    // A blob that must go to the device and fits the kernel's arguments
+    // travels in them: the launch reads no host memory and needs no
+    // staging slot.
+    if (pool->rows.size() <= static_cast<size_t>(pkv::kIntChunk) &&
+        (!pool->dev.holds(kRows, key) || !pool->meta.patches().empty())) {
+      if (pool->checks > 0)
+        if (int32_t rc = check_blob(pool, seqs, M, pool->rows, pool->patch_off)) return rc;
+      const int32_t n_blob = static_cast<int32_t>(pool->rows.size());
+      const int32_t n_patch = static_cast<int32_t>((n_blob - pool->patch_off) / 3);
+      int32_t* d = nullptr;
+      if (pool->dev.claim(kRows, n_blob * sizeof(int32_t), key, st, &d) != hipSuccess)
+        return PKV_ERR_DEVICE;
+      pool->meta.patches().clear();
+      pool->rows_key = key;
+      pool->dev.form[PKV_K_APPEND] = std::string("append_inline_kernel<") +
+                                     (span_of(pool) % 4 == 0 ? "4" : "1") + ", " +
+                                     (pool->rope ? "true" : "false") + ">";
+      hipError_t e;
+      {
+        DeviceCtx::ProfScope ps(&pool->dev, PKV_K_APPEND, st);
+        e = pkv::launch_append_inline(pm, K_new_dev, V_new_dev, M, kv_dim,
+                                      pool->meta.head_dim(), rope_table(pool->rope),
+                                      pool->mirror, pool->stride, d, pool->rows.data(),
+                                      n_blob, static_cast<int32_t>(pool->patch_off), n_patch,
+                                      st);
+      }
+      if (e != hipSuccess) {  // the device blob was never written
+        pool->dev.buf[kRows].valid = false;
+        pool->rows_key.clear();
+      }
+      return dev_status(e);
+    }
+  }
   pkv::PatchArgs pa{};
-  if (pool_rows(pool, seqs, M, n_new, shared_heads, st, &rows,
-                n_new == 1 ? &pa : nullptr) != hipSuccess)
+  if (rows_to_device(pool, key, st, &rows, n_new == 1 ? &pa : nullptr) != hipSuccess)
     return PKV_ERR_DEVICE;
   if (pool->checks > 0)
     if (int32_t rc = check_blob(pool, seqs, M, pool->rows, pool->patch_off)) return rc;
-  const PagedMap pm = make_paged_map(pool, layer);
-  const int32_t kv_dim = pool->meta.n_kv_heads() * pool->meta.head_dim();
-  const int32_t span = pool->rope ? pool->meta.head_dim() / 2 : pool->meta.head_dim();
   pool->dev.form[PKV_K_APPEND] = std::string("append_kernel<") +
-                                 (span % 4 == 0 ? "4" : "1") + ", PagedMap, " +
+                                 (span_of(pool) % 4 == 0 ? "4" : "1") + ", PagedMap, " +
                                  (pool->rope ? "true" : "false") + ", " +
                                  (n_new == 1 ? "true" : "false") + ">";
   if (n_new == 1) {

@@ -182,6 +182,15 @@ hipError_t launch_append_one(const PagedMap& m, const RowDesc* rows,
                              int32_t kv_dim, int32_t head_dim,
                              const double2* rope, const PatchArgs& pa,
                              hipStream_t st);
+// The same with the row blob (n_blob <= kIntChunk ints) passed in the kernel
+// arguments: the launch reads the rows' descriptors and the patches (n_patch
+// triples from int patch_off) from its argument copy, applies the patches
+// and stores the blob to blob_dst.
+hipError_t launch_append_inline(const PagedMap& m, const float* K, const float* V,
+                                int32_t M, int32_t kv_dim, int32_t head_dim,
+                                const double2* rope, int32_t* mirror, int64_t stride,
+                                int32_t* blob_dst, const int32_t* blob, int32_t n_blob,
+                                int32_t patch_off, int32_t n_patch, hipStream_t st);
 hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,
                       int64_t block_floats, hipStream_t st);
 // deep: two pages in flight per wave (one wave per SIMD for group 4 and 8)

@@ -116,21 +116,16 @@ __device__ __forceinline__ void rotate_pair(float& lo, float& hi,
 // of a head and the VEC floats they pair with in the second half, and turns
 // the K pairs by the row's position before storing them (V is stored as is).
 // ---------------------------------------------------------------------------
-// ONE: one new row per sequence, written to the RowDesc's append_block (no
-// page-table read), while the first threads apply the pending mirror patches.
+// The scatter of rows [r][t] (element e of the flattened [rows][n][units]
+// grid), from K / V into the pool.  ONE: one new row per sequence, written to
+// the RowDesc's append_block (no page-table read).
 template <int VEC, class Map, bool ROPE, bool ONE>
-__global__ __launch_bounds__(256) void append_kernel(
-    Map m, const RowDesc* __restrict__ rows, const float* __restrict__ K,
+__device__ __forceinline__ void append_elems(
+    const Map& m, const RowDesc* __restrict__ rows, const float* __restrict__ K,
     const float* __restrict__ V, int32_t n, int32_t kv_dim, int32_t head_dim,
-    int64_t total, const double2* __restrict__ cs, PatchArgs pa) {
+    int64_t total, const double2* __restrict__ cs) {
   const int32_t span = ROPE ? head_dim / 2 : head_dim;  // floats per head unit
   const int32_t per_row = (ROPE ? kv_dim / 2 : kv_dim) / VEC;
-  if constexpr (ONE) {
-    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (i < pa.n)
-      pa.mirror[pa.patches[3 * i] * pa.stride + pa.patches[3 * i + 1]] = pa.patches[3 * i + 2];
-    if (i < pa.n_copy) pa.copy_dst[i] = pa.copy_src[i];
-  }
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t rt = e / per_row;
@@ -185,6 +180,51 @@ __global__ __launch_bounds__(256) void append_kernel(
       dst[m.v_off] = V[src];
     }
   }
+}
+
+// ONE: one new row per sequence, written to the RowDesc's append_block (no
+// page-table read), while the first threads apply the pending mirror patches
+// and copy the row blob.
+template <int VEC, class Map, bool ROPE, bool ONE>
+__global__ __launch_bounds__(256) void append_kernel(
+    Map m, const RowDesc* __restrict__ rows, const float* __restrict__ K,
+    const float* __restrict__ V, int32_t n, int32_t kv_dim, int32_t head_dim,
+    int64_t total, const double2* __restrict__ cs, PatchArgs pa) {
+  if constexpr (ONE) {
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i < pa.n)
+      pa.mirror[pa.patches[3 * i] * pa.stride + pa.patches[3 * i + 1]] = pa.patches[3 * i + 2];
+    if (i < pa.n_copy) pa.copy_dst[i] = pa.copy_src[i];
+  }
+  append_elems<VEC, Map, ROPE, ONE>(m, rows, K, V, n, kv_dim, head_dim, total, cs);
+}
+
+// Ints passed by value as kernel arguments (array first: 16-byte aligned, so
+// RowDesc records in it load as whole vectors).
+struct alignas(16) IntChunk {
+  int32_t v[kIntChunk];
+  int32_t n;
+};
+
+// The one-row append with the step's row blob in the kernel arguments
+// (blobs of up to kIntChunk ints): descriptors and patches are read from the
+// argument copy -- no read of host memory -- and the first threads store the
+// blob to blob_dst for the launches that follow and apply the patches
+// (n_patch triples from int patch_off of the blob).
+template <int VEC, bool ROPE>
+__global__ __launch_bounds__(256) void append_inline_kernel(
+    PagedMap m, const float* __restrict__ K, const float* __restrict__ V,
+    int32_t kv_dim, int32_t head_dim, int64_t total, const double2* __restrict__ cs,
+    int32_t* mirror, int64_t stride, int32_t patch_off, int32_t n_patch,
+    int32_t* blob_dst, IntChunk b) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n_patch) {
+    const int32_t* pt = b.v + patch_off + 3 * i;
+    mirror[pt[0] * stride + pt[1]] = pt[2];
+  }
+  if (i < b.n) blob_dst[i] = b.v[i];
+  append_elems<VEC, PagedMap, ROPE, true>(m, reinterpret_cast<const RowDesc*>(b.v), K, V, 1,
+                                          kv_dim, head_dim, total, cs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1493,11 +1533,6 @@ hipError_t prefill_impl(const Map& m, const AttnArgs& a, int32_t group,
 // library never allocates at run time: the code object carries it, and each
 // GPU gets its own copy when the library's kernels are loaded there.
 // ---------------------------------------------------------------------------
-struct IntChunk {
-  int32_t n;
-  int32_t v[kIntChunk];
-};
-
 __global__ __launch_bounds__(256) void write_ints_kernel(int32_t* dst, IntChunk c) {
   const int32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < c.n) dst[i] = c.v[i];
@@ -1564,6 +1599,44 @@ hipError_t launch_append_one(const PagedMap& m, const RowDesc* rows,
                              hipStream_t st) {
   return append_impl<PagedMap, true>(m, rows, K, V, M, 1, kv_dim, head_dim, rope, pa,
                                      st);
+}
+
+hipError_t launch_append_inline(const PagedMap& m, const float* K, const float* V,
+                                int32_t M, int32_t kv_dim, int32_t head_dim,
+                                const double2* rope, int32_t* mirror, int64_t stride,
+                                int32_t* blob_dst, const int32_t* blob, int32_t n_blob,
+                                int32_t patch_off, int32_t n_patch, hipStream_t st) {
+  if (n_blob < 0 || n_blob > kIntChunk || patch_off < 0 ||
+      (int64_t)patch_off + 3 * (int64_t)n_patch > n_blob)
+    return hipErrorInvalidValue;
+  const bool rope_on = rope != nullptr;
+  if (rope_on && head_dim % 2 != 0) return hipErrorInvalidValue;
+  const int32_t span = rope_on ? head_dim / 2 : head_dim;
+  const bool vec = (span % 4 == 0);
+  const int64_t total = (int64_t)M * (rope_on ? kv_dim / 2 : kv_dim) / (vec ? 4 : 1);
+  const int64_t want = (std::max<int64_t>({total, n_patch, n_blob}) + 255) / 256;
+  const int grid = static_cast<int>(want < 65536 ? (want > 0 ? want : 1) : 65536);
+  if ((int64_t)grid * 256 < n_blob) return hipErrorInvalidValue;
+  IntChunk c;
+  c.n = n_blob;
+  std::copy(blob, blob + n_blob, c.v);
+  if (rope_on && vec)
+    append_inline_kernel<4, true><<<grid, 256, 0, st>>>(m, K, V, kv_dim, head_dim, total, rope,
+                                                         mirror, stride, patch_off, n_patch,
+                                                         blob_dst, c);
+  else if (rope_on)
+    append_inline_kernel<1, true><<<grid, 256, 0, st>>>(m, K, V, kv_dim, head_dim, total, rope,
+                                                         mirror, stride, patch_off, n_patch,
+                                                         blob_dst, c);
+  else if (vec)
+    append_inline_kernel<4, false><<<grid, 256, 0, st>>>(m, K, V, kv_dim, head_dim, total,
+                                                          rope, mirror, stride, patch_off,
+                                                          n_patch, blob_dst, c);
+  else
+    append_inline_kernel<1, false><<<grid, 256, 0, st>>>(m, K, V, kv_dim, head_dim, total,
+                                                          rope, mirror, stride, patch_off,
+                                                          n_patch, blob_dst, c);
+  return hipGetLastError();
 }
 
 hipError_t launch_cow(float* base, const int32_t* pairs, int32_t n_pairs,

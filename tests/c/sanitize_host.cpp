@@ -73,6 +73,11 @@ hipError_t launch_append_one(const PagedMap&, const RowDesc*, const float*, cons
                              hipStream_t) {
   no_device("launch_append_one");
 }
+hipError_t launch_append_inline(const PagedMap&, const float*, const float*, int32_t, int32_t,
+                                int32_t, const double2*, int32_t*, int64_t, int32_t*,
+                                const int32_t*, int32_t, int32_t, int32_t, hipStream_t) {
+  no_device("launch_append_inline");
+}
 hipError_t launch_cow(float*, const int32_t*, int32_t, int64_t, hipStream_t) {
   no_device("launch_cow");
 }

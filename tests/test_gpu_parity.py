@@ -543,5 +543,77 @@ def test_kernel_forms_recorded():
     decode_step(pool, seqs, q, k, v, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.scale)
     assert pool.kernel_name(pkv.K_DECODE) == "decode_fast_kernel<4, PagedMap, false>"
     assert pool.kernel_name(pkv.K_MERGE) == "merge_kernel"
-    assert pool.kernel_name(pkv.K_APPEND) == "append_kernel<4, PagedMap, false, true>"
+    # the 32-row blob fits the append kernel's arguments
+    assert pool.kernel_name(pkv.K_APPEND) == "append_inline_kernel<4, false>"
+    pool.close()
+
+
+def test_mirror_growth_then_multirow_append():
+    """A sequence created after earlier device calls with a longer max_tokens
+    makes the next call grow (reallocate) the page-table mirror; the
+    multi-row append of that call must address pages through the new mirror.
+    Outputs of both sequences against the oracle."""
+    H, G, D, B = 32, 8, 128, 16
+    rng = np.random.default_rng(91)
+    pool = pkv.Pool(400, B, 1, G, D, max_seqs=4)
+    scale = float(np.float32(1 / np.sqrt(D)))
+    s0 = pool.seq_new(40)
+    k0 = rng.standard_normal((20, G * D)).astype(np.float32)
+    v0 = rng.standard_normal((20, G * D)).astype(np.float32)
+    pool.ensure_append([s0], 20, check=True)
+    pool.append_layer([s0], 20, 0, dev(k0), dev(v0), check=True)
+    pool.advance([s0], 20, check=True)
+    s1 = pool.seq_new(5000)  # 313 pages: the mirror's stride grows
+    k1 = rng.standard_normal((700, G * D)).astype(np.float32)
+    v1 = rng.standard_normal((700, G * D)).astype(np.float32)
+    pool.ensure_append([s1], 700, check=True)
+    pool.append_layer([s1], 700, 0, dev(k1), dev(v1), check=True)
+    pool.advance([s1], 700, check=True)
+    q = rng.standard_normal((2, H * D)).astype(np.float32)
+    k = rng.standard_normal((2, G * D)).astype(np.float32)
+    v = rng.standard_normal((2, G * D)).astype(np.float32)
+    out = decode_step(pool, [s0, s1], q, k, v, H, G, D, scale).cpu().numpy()
+    for r, (hk, hv) in enumerate(((k0, v0), (k1, v1))):
+        rc, ref = oracle.attn_contig(q[r:r + 1], np.concatenate([hk, k[r:r + 1]]),
+                                     np.concatenate([hv, v[r:r + 1]]), H, G, D, True, scale)
+        assert rc == 0
+        assert_close(out[r:r + 1], ref, "row %d" % r)
+    pool.close()
+
+
+def test_one_row_append_staged_blob_matches_oracle():
+    """A batch whose row blob is too large for the append kernel's arguments
+    (200 sequences: 1600 ints of row descriptors) takes the staged one-row
+    append; two steps of it against the oracle."""
+    H, G, D, B = 32, 8, 128, 16
+    rng = np.random.default_rng(77)
+    lens = rng.integers(1, 40, size=200)
+    pool = pkv.Pool(int(sum((l + 2) // B + 2 for l in lens)) + 8, B, 1, G, D, max_seqs=208)
+    seqs = [pool.seq_new(64) for _ in lens]
+    hist = []
+    for s_, l in zip(seqs, lens):
+        k = rng.standard_normal((l, G * D)).astype(np.float32)
+        v = rng.standard_normal((l, G * D)).astype(np.float32)
+        pool.ensure_append([s_], int(l), check=True)
+        pool.append_layer([s_], int(l), 0, dev(k), dev(v), check=True)
+        pool.advance([s_], int(l), check=True)
+        hist.append((k, v))
+    scale = float(np.float32(1 / np.sqrt(D)))
+    for step in range(2):
+        q = rng.standard_normal((len(seqs), H * D)).astype(np.float32)
+        k = rng.standard_normal((len(seqs), G * D)).astype(np.float32)
+        v = rng.standard_normal((len(seqs), G * D)).astype(np.float32)
+        out = decode_step(pool, seqs, q, k, v, H, G, D, scale).cpu().numpy()
+        assert pool.kernel_name(pkv.K_APPEND) == "append_kernel<4, PagedMap, false, true>"
+        for r in range(0, len(seqs), 7):
+            hk = np.concatenate([hist[r][0], k[r:r + 1]])
+            hv = np.concatenate([hist[r][1], v[r:r + 1]])
+            rc, ref = oracle.attn_contig(q[r:r + 1], hk, hv, H, G, D, True, scale)
+            assert rc == 0
+            assert_close(out[r:r + 1], ref, "step %d row %d" % (step, r))
+            hist[r] = (hk, hv)
+        for r in range(len(seqs)):
+            if r % 7:
+                hist[r] = (np.concatenate([hist[r][0], k[r:r + 1]]),
+                           np.concatenate([hist[r][1], v[r:r + 1]]))
     pool.close()
