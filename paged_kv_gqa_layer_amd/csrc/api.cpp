@@ -526,6 +526,9 @@ struct pkv_pool {
   DeviceCtx dev;
   int32_t* mirror = nullptr;  // [max_seqs][stride]
   int64_t stride = 0;
+  // A launch that was to apply page-table patches (taken off the pending
+  // list) failed: the next call re-patches every entry of every table.
+  bool mirror_stale = false;
   // the row blob currently in dev.buf[kRows]
   std::vector<int32_t> rows;
   std::vector<int32_t> na_rows;  // the last zero-allocation decode's blob
@@ -549,20 +552,11 @@ struct pkv_pool {
 
 namespace {
 
-// (Re)allocate the page-table mirror when a sequence may outgrow its stride;
-// a new mirror is filled from every live page-table entry.
-hipError_t size_mirror(pkv_pool* p, hipStream_t st) {
+// Every page-table entry of every sequence as a pending patch (a new or
+// stale mirror), replacing the pending list.
+void queue_all_pages(pkv_pool* p) {
   auto& m = p->meta;
-  const int64_t stride = pkv::PoolMeta::mirror_stride(m.max_pages_seen());
-  if (p->mirror && stride <= p->stride) return hipSuccess;
-  hipError_t e;
-  if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
-  if (p->mirror) (void)hipFree(p->mirror);
-  p->mirror = nullptr;
-  if ((e = hipMalloc(&p->mirror, static_cast<size_t>(m.max_seqs()) * stride *
-                                     sizeof(int32_t))) != hipSuccess)
-    return e;
-  p->stride = stride;
+  p->mirror_stale = false;
   p->rows_key.clear();  // row descriptors hold mirror offsets
   auto& pt = m.patches();
   pt.clear();
@@ -572,6 +566,26 @@ hipError_t size_mirror(pkv_pool* p, hipStream_t st) {
     for (int32_t i = 0; i < static_cast<int32_t>(q->pages.size()); ++i)
       pt.push_back({s, i, q->pages[i]});
   }
+}
+
+// (Re)allocate the page-table mirror when a sequence may outgrow its stride;
+// a new or stale mirror is filled from every live page-table entry.
+hipError_t size_mirror(pkv_pool* p, hipStream_t st) {
+  auto& m = p->meta;
+  const int64_t stride = pkv::PoolMeta::mirror_stride(m.max_pages_seen());
+  const bool grow = !p->mirror || stride > p->stride;
+  if (!grow && !p->mirror_stale) return hipSuccess;
+  if (grow) {
+    hipError_t e;
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+    if (p->mirror) (void)hipFree(p->mirror);
+    p->mirror = nullptr;
+    if ((e = hipMalloc(&p->mirror, static_cast<size_t>(m.max_seqs()) * stride *
+                                       sizeof(int32_t))) != hipSuccess)
+      return e;
+    p->stride = stride;
+  }
+  queue_all_pages(p);
   return hipSuccess;
 }
 
@@ -673,8 +687,10 @@ hipError_t rows_to_device(pkv_pool* p, const std::vector<int64_t>& key, hipStrea
   if (!pt.empty()) {
     pt.clear();
     if ((e = pkv::launch_patch(p->mirror, d + p->patch_off, n_patch, p->stride, st)) !=
-        hipSuccess)
+        hipSuccess) {
+      p->mirror_stale = true;
       return e;
+    }
   }
   p->rows_key = key;
   *rows_dev = d;
@@ -1170,9 +1186,10 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
                                       n_blob, static_cast<int32_t>(pool->patch_off), n_patch,
                                       st);
       }
-      if (e != hipSuccess) {  // the device blob was never written
+      if (e != hipSuccess) {  // neither the blob nor the patches reached the device
         pool->dev.buf[kRows].valid = false;
         pool->rows_key.clear();
+        pool->mirror_stale = true;
       }
       return dev_status(e);
     }
@@ -1195,9 +1212,10 @@ int32_t pkv_append_layer(pkv_pool* pool, const int32_t* seqs, int32_t M,
                                  rope_table(pool->rope), pa, st);
     }
     if (e == hipSuccess && pa.n_copy > 0) e = pool->dev.staged(st);
-    if (e != hipSuccess) {  // the device blob was never written
+    if (e != hipSuccess) {  // neither the blob nor the patches reached the device
       pool->dev.buf[kRows].valid = false;
       pool->rows_key.clear();
+      if (pa.n > 0) pool->mirror_stale = true;
     }
     return dev_status(e);
   }
@@ -1400,6 +1418,7 @@ int32_t pkv_attn_paged_decode_noalloc(pkv_pool* pool, const int32_t* seqs, int32
     return PKV_ERR_UNSUPPORTED;
   if (pool->checks > 0)
     if (int32_t rc = check_state(pool, seqs, M, 1, false)) return rc;
+  if (pool->mirror_stale) queue_all_pages(pool);  // host work only
   RowPlan plan;
   size_t patch_off = 0;
   build_blob(pool, seqs, M, 1, 0, pool->na_rows, &plan, &patch_off);
