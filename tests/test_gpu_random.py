@@ -48,7 +48,14 @@ def _turn(x, heads, D, pos, rope):
     return y
 
 
-@pytest.mark.parametrize("seed", range(180))
+def _seeds():
+    """range(180), or PKV_RANDOM_SEEDS="lo:hi" for a wider campaign."""
+    import os
+    lo, _, hi = os.environ.get("PKV_RANDOM_SEEDS", "0:180").partition(":")
+    return range(int(lo), int(hi))
+
+
+@pytest.mark.parametrize("seed", _seeds())
 def test_random_case(seed):
     rng, H, G, D, B, kind, M, n_q, rope, lens = _case(1000 + seed)
     scale = float(np.float32(1 / math.sqrt(D)))
